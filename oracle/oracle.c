@@ -1,0 +1,315 @@
+/*
+ * CPU oracle for MLRA decode attention over a paged latent cache.
+ *
+ * TEST INFRASTRUCTURE ONLY: called by the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the product path. It shares no
+ * code with the HIP library.
+ *
+ * Sources (the pages this follows):
+ *  - "Multi-Head Latent Attention" concept page (ai360xpert), "The two
+ *    projections": the cache keeps c = W^DKV x per token; per-head keys and
+ *    values are rebuilt as K_h = W^UK_h c and V_h = W^UV_h c. "Show Me the
+ *    Code" stores the up-projections as (H, d_c, d_head).
+ *  - "Multi-Head Latent Attention (MLA): How Low-Rank KV Compression Crushes
+ *    Transformer Memory Footprints by 93%" (lesty.tech), section 4 "The
+ *    Decoupled RoPE Mechanism": the attention logit is the content dot product
+ *    plus the dot product of the query's RoPE part with a d_r-wide key that all
+ *    heads share; the cache holds [c, k^R]. Section 5 "On-The-Fly Matrix
+ *    Absorption": q W^UK^T against raw c, and the value up-projection applied
+ *    once to the softmax-weighted latent sum.
+ *  - "Multi-Head Low-Rank Attention: Making Compressed Attention Actually
+ *    Parallelizable" (alanhou.org), "Core Mechanism" and "Key Concepts": the
+ *    latent is split into independent latent heads, each serving a subset of
+ *    the query heads, with per-subset attention whose results are combined.
+ *  - "Multi-Head Low-Rank Attention" paper page (thelatestinai.com), Table 1
+ *    (cache and loading per token per device) and Table 2 (decode arithmetic
+ *    intensity): the counters at the end of this file.
+ *
+ * Readings where the pages leave a step open (all listed with reasons in the
+ * repository's design notes): softmax scale 1/sqrt(d_h + d_r); head i of h
+ * reads blocks J(i) = {g k + jj : jj < k} with g = i / (h k / b); each
+ * attended block has its own softmax and the per-block outputs are summed
+ * times out_scale (1/sqrt(k), which is 1 when k = 1); an empty sequence gives
+ * a zero output and lse = -inf.
+ *
+ * parity pins: every function here is pinned by tests/test_oracle_*.py
+ * (closed forms, brute force, textbook attention, Table 1 / Table 2 values).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- elements */
+
+static double elem(int32_t dtype, const void* base, int64_t idx) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  return (double)((const float*)base)[idx];
+}
+
+uint16_t oracle_round_bf16(double v) {
+  /* bf16 keeps 8 significant bits. Scale the magnitude so those bits are the
+   * integer part, round half to even with rint (default rounding mode), scale
+   * back: the result is exactly representable in fp32, whose top half is the
+   * bf16 pattern. */
+  if (v != v) return 0x7FC0;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  double m = frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+  double r = ldexp(rint(ldexp(m, 8)), e - 8);
+  float f = (float)r;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u >> 16) | sign);
+}
+
+static void store_elem(int32_t dtype, void* base, int64_t idx, double v) {
+  if (dtype == ORACLE_BF16)
+    ((uint16_t*)base)[idx] = oracle_round_bf16(v);
+  else
+    ((float*)base)[idx] = (float)v;
+}
+
+/* ------------------------------------------------------------------ shape */
+
+static double scale_of(const oracle_shape* s) {
+  return s->softmax_scale > 0 ? s->softmax_scale : 1.0 / sqrt((double)(s->d_h + s->d_r));
+}
+
+static double out_scale_of(const oracle_shape* s) {
+  return s->out_scale > 0 ? s->out_scale : 1.0 / sqrt((double)s->blocks_per_head);
+}
+
+int32_t oracle_block_of(const oracle_shape* s, int32_t head, int32_t jj) {
+  /* b / k head groups; each group owns k consecutive blocks and h k / b heads. */
+  int32_t heads_per_group = s->n_heads * s->blocks_per_head / s->n_blocks;
+  int32_t group = head / heads_per_group;
+  return group * s->blocks_per_head + jj;
+}
+
+int64_t oracle_row_index(const oracle_shape* s, const int32_t* page_table, int32_t b, int32_t t) {
+  int32_t logical_page = t / s->page_size;
+  int32_t offset = t % s->page_size;
+  int64_t phys = page_table ? (int64_t)page_table[(int64_t)b * s->max_pages_per_seq + logical_page]
+                            : (int64_t)b * s->max_pages_per_seq + logical_page;
+  return phys * s->page_size + offset;
+}
+
+/* ------------------------------------------------------ un-absorbed decode */
+
+void oracle_decode_unabsorbed(const oracle_shape* s, const void* pool, const int32_t* page_table,
+                              const int32_t* seq_lens, const void* q_c, const void* q_r,
+                              const void* w_uk, const void* w_uv, int32_t npairs,
+                              const int32_t* pair_b, const int32_t* pair_head, double* out,
+                              double* lse) {
+  const int32_t H = s->n_heads, DH = s->d_h, DR = s->d_r, K = s->blocks_per_head;
+  const int32_t W = s->d_c / s->n_blocks;
+  const int32_t ROW = s->d_c + s->d_r;
+  const double sigma = scale_of(s), alpha = out_scale_of(s);
+  const int32_t dt = s->dtype;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t p = 0; p < npairs; ++p) {
+    const int32_t b = pair_b[p], i = pair_head[p];
+    const int32_t n = seq_lens[b];
+    double* o = out + (int64_t)p * DH;
+    for (int32_t d = 0; d < DH; ++d) o[d] = 0.0;
+    if (n <= 0) {
+      for (int32_t jj = 0; jj < K; ++jj) lse[(int64_t)p * K + jj] = -INFINITY;
+      continue;
+    }
+    double* q = (double*)malloc(sizeof(double) * (DH + DR));
+    double* wk = (double*)malloc(sizeof(double) * (size_t)W * DH);
+    double* wv = (double*)malloc(sizeof(double) * (size_t)W * DH);
+    double* c = (double*)malloc(sizeof(double) * W);
+    double* kvec = (double*)malloc(sizeof(double) * DH);
+    double* score = (double*)malloc(sizeof(double) * n);
+    for (int32_t d = 0; d < DH; ++d) q[d] = elem(dt, q_c, ((int64_t)b * H + i) * DH + d);
+    for (int32_t r = 0; r < DR; ++r) q[DH + r] = elem(dt, q_r, ((int64_t)b * H + i) * DR + r);
+
+    for (int32_t jj = 0; jj < K; ++jj) {
+      const int32_t j = oracle_block_of(s, i, jj);
+      const int64_t wbase = ((int64_t)i * K + jj) * W * DH;
+      for (int64_t e = 0; e < (int64_t)W * DH; ++e) {
+        wk[e] = elem(dt, w_uk, wbase + e);
+        wv[e] = elem(dt, w_uv, wbase + e);
+      }
+      /* pass 1: reconstruct the key of every token and score it */
+      double m = -INFINITY;
+      for (int32_t t = 0; t < n; ++t) {
+        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
+        for (int32_t cc = 0; cc < W; ++cc) c[cc] = elem(dt, pool, row + (int64_t)j * W + cc);
+        for (int32_t d = 0; d < DH; ++d) kvec[d] = 0.0;
+        for (int32_t cc = 0; cc < W; ++cc) /* K_t = W^UK_{i,j}^T c_{t,j} */
+          for (int32_t d = 0; d < DH; ++d) kvec[d] += wk[(int64_t)cc * DH + d] * c[cc];
+        double content = 0.0, rope = 0.0;
+        for (int32_t d = 0; d < DH; ++d) content += q[d] * kvec[d];
+        for (int32_t r = 0; r < DR; ++r) rope += q[DH + r] * elem(dt, pool, row + s->d_c + r);
+        score[t] = sigma * (content + rope);
+        if (score[t] > m) m = score[t];
+      }
+      /* pass 2: softmax weights, reconstruct every value, accumulate */
+      double denom = 0.0;
+      for (int32_t t = 0; t < n; ++t) denom += exp(score[t] - m);
+      for (int32_t t = 0; t < n; ++t) {
+        const double pt = exp(score[t] - m) / denom;
+        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
+        for (int32_t cc = 0; cc < W; ++cc) c[cc] = elem(dt, pool, row + (int64_t)j * W + cc);
+        for (int32_t d = 0; d < DH; ++d) kvec[d] = 0.0; /* reused as V_t */
+        for (int32_t cc = 0; cc < W; ++cc)
+          for (int32_t d = 0; d < DH; ++d) kvec[d] += wv[(int64_t)cc * DH + d] * c[cc];
+        for (int32_t d = 0; d < DH; ++d) o[d] += alpha * pt * kvec[d];
+      }
+      lse[(int64_t)p * K + jj] = m + log(denom);
+    }
+    free(q); free(wk); free(wv); free(c); free(kvec); free(score);
+  }
+}
+
+/* -------------------------------------------------------- absorbed decode */
+
+void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32_t* page_table,
+                            const int32_t* seq_lens, const void* q_c, const void* q_r,
+                            const void* w_uk, const void* w_uv, int32_t npairs,
+                            const int32_t* pair_b, const int32_t* pair_head, double* out,
+                            double* lse) {
+  const int32_t H = s->n_heads, DH = s->d_h, DR = s->d_r, K = s->blocks_per_head;
+  const int32_t W = s->d_c / s->n_blocks;
+  const int32_t ROW = s->d_c + s->d_r;
+  const double sigma = scale_of(s), alpha = out_scale_of(s);
+  const int32_t dt = s->dtype;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t p = 0; p < npairs; ++p) {
+    const int32_t b = pair_b[p], i = pair_head[p];
+    const int32_t n = seq_lens[b];
+    double* o = out + (int64_t)p * DH;
+    for (int32_t d = 0; d < DH; ++d) o[d] = 0.0;
+    if (n <= 0) {
+      for (int32_t jj = 0; jj < K; ++jj) lse[(int64_t)p * K + jj] = -INFINITY;
+      continue;
+    }
+    double* qt = (double*)malloc(sizeof(double) * W);   /* W^UK^T q, in latent space */
+    double* acc = (double*)malloc(sizeof(double) * W);  /* sum_t p_t c_t */
+    double* score = (double*)malloc(sizeof(double) * n);
+    for (int32_t jj = 0; jj < K; ++jj) {
+      const int32_t j = oracle_block_of(s, i, jj);
+      const int64_t wbase = ((int64_t)i * K + jj) * W * DH;
+      for (int32_t cc = 0; cc < W; ++cc) {
+        double v = 0.0;
+        for (int32_t d = 0; d < DH; ++d)
+          v += elem(dt, w_uk, wbase + (int64_t)cc * DH + d) * elem(dt, q_c, ((int64_t)b * H + i) * DH + d);
+        qt[cc] = v;
+      }
+      double m = -INFINITY;
+      for (int32_t t = 0; t < n; ++t) {
+        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
+        double v = 0.0;
+        for (int32_t cc = 0; cc < W; ++cc) v += qt[cc] * elem(dt, pool, row + (int64_t)j * W + cc);
+        for (int32_t r = 0; r < DR; ++r)
+          v += elem(dt, q_r, ((int64_t)b * H + i) * DR + r) * elem(dt, pool, row + s->d_c + r);
+        score[t] = sigma * v;
+        if (score[t] > m) m = score[t];
+      }
+      double denom = 0.0;
+      for (int32_t t = 0; t < n; ++t) denom += exp(score[t] - m);
+      for (int32_t cc = 0; cc < W; ++cc) acc[cc] = 0.0;
+      for (int32_t t = 0; t < n; ++t) {
+        const double pt = exp(score[t] - m) / denom;
+        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
+        for (int32_t cc = 0; cc < W; ++cc) acc[cc] += pt * elem(dt, pool, row + (int64_t)j * W + cc);
+      }
+      for (int32_t d = 0; d < DH; ++d) {
+        double v = 0.0;
+        for (int32_t cc = 0; cc < W; ++cc) v += elem(dt, w_uv, wbase + (int64_t)cc * DH + d) * acc[cc];
+        o[d] += alpha * v;
+      }
+      lse[(int64_t)p * K + jj] = m + log(denom);
+    }
+    free(qt); free(acc); free(score);
+  }
+}
+
+/* ----------------------------------------------------------------- append */
+
+void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
+                   const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
+                   void* c_out) {
+  const int32_t DC = s->d_c, DR = s->d_r, DM = s->d_model, ROW = s->d_c + s->d_r;
+  const int32_t dt = s->dtype;
+  for (int32_t b = 0; b < s->batch; ++b) {
+    const int64_t row = oracle_row_index(s, page_table, b, positions[b]) * ROW;
+    for (int32_t cc = 0; cc < DC; ++cc) {
+      double v = 0.0; /* c = x W^DKV, W^DKV stored [d_model][d_c] */
+      for (int32_t m = 0; m < DM; ++m)
+        v += elem(dt, x, (int64_t)b * DM + m) * elem(dt, w_dkv, (int64_t)m * DC + cc);
+      store_elem(dt, pool, row + cc, v);
+      if (c_out) store_elem(dt, c_out, (int64_t)b * DC + cc, v);
+    }
+    for (int32_t r = 0; r < DR; ++r)
+      store_elem(dt, pool, row + DC + r, elem(dt, kr_new, (int64_t)b * DR + r));
+  }
+}
+
+/* --------------------------------------------------------------- counters */
+
+double oracle_cache_elems_per_token(int32_t method, int32_t h, int32_t d_h, int32_t g,
+                                    int32_t beta_kv, int32_t d_c, int32_t d_r) {
+  switch (method) {
+    case 0: return 2.0 * h * d_h;                     /* MHA: K and V of every head */
+    case 1: return 2.0 * d_h;                         /* MQA: one shared K/V head */
+    case 2: return 2.0 * g * d_h;                     /* GQA: one K/V head per group */
+    case 3: return (double)d_c + d_r;                 /* MLA: latent + shared RoPE key */
+    case 4: return 2.0 * 2.0 * d_h;                   /* MFA: one K/V head of width 2 d_h */
+    case 5: return 2.0 * beta_kv * ((double)h + d_h); /* TPA: rank-beta_kv factors of K and V */
+    case 6: return (double)d_c + d_r;                 /* MLRA: the blocks together are d_c wide */
+    default: return -1.0;
+  }
+}
+
+double oracle_cache_elems_per_device(int32_t method, int32_t h, int32_t d_h, int32_t g,
+                                     int32_t beta_kv, int32_t d_c, int32_t d_r,
+                                     int32_t n_blocks, int32_t tp) {
+  /* Tensor parallelism over heads: whatever is per-head is split, whatever is
+   * shared by all heads is replicated on every device. */
+  switch (method) {
+    case 0: return 2.0 * ((double)h / tp) * d_h;
+    case 1: return 2.0 * d_h;
+    case 2: return 2.0 * ((double)g / (tp < g ? tp : g)) * d_h;
+    case 3: return (double)d_c + d_r;
+    case 4: return 2.0 * 2.0 * d_h;
+    case 5: return 2.0 * beta_kv * ((double)h / tp + d_h);
+    case 6: { /* each device holds its share of the latent blocks plus the RoPE key */
+      int32_t shards = tp < n_blocks ? tp : n_blocks;
+      return (double)d_c / shards + d_r;
+    }
+    default: return -1.0;
+  }
+}
+
+void oracle_decode_flops_bytes(double n, double heads_u, double w_u, double d_r,
+                               double elem_bytes, double* flops, double* bytes) {
+  /* per token and head: score q~ . c (2 w_u) + q^R . k^R (2 d_r), weighted sum
+   * p c (2 w_u); every cached element of the unit is loaded once per token. */
+  *flops = n * heads_u * (2.0 * (w_u + d_r) + 2.0 * w_u);
+  *bytes = elem_bytes * n * (w_u + d_r);
+}
+
+int32_t oracle_num_threads(void) {
+#ifdef _OPENMP
+  return (int32_t)omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
