@@ -1,0 +1,254 @@
+"""Python binding of libmlra: MLRA decode attention over a paged latent cache
+on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libmlra.so,
+reached through its C ABI (include/mlra.h) with ctypes. PyTorch provides device
+memory and streams. There is no CPU fallback: importing works anywhere, but
+every call raises if the library is not built or no GPU is present.
+
+Entry points (same names as the C ABI, without the mlra_ prefix):
+  workspace_bytes, append_latent, absorb_query, attend, decode, combine,
+  read_flags, status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmlra.so")
+
+F32, BF16 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+FLAG_BAD_PAGE = 1
+ABI_VERSION = 1
+
+
+class MlraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class MlraDesc(ctypes.Structure):
+    """Mirror of mlra_desc (include/mlra.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_h", ctypes.c_int32),
+        ("d_c", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("blocks_per_head", ctypes.c_int32),
+        ("d_r", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("d_model", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("out_scale", ctypes.c_float),
+    ]
+
+
+def make_desc(batch, n_heads, d_h, d_c, n_blocks, d_r, max_pages_per_seq, num_pages, dtype,
+              page_size=64, blocks_per_head=1, d_model=0, softmax_scale=0.0, out_scale=0.0) -> MlraDesc:
+    if isinstance(dtype, str):
+        dtype = {"f32": F32, "bf16": BF16}[dtype]
+    return MlraDesc(batch=batch, n_heads=n_heads, d_h=d_h, d_c=d_c, n_blocks=n_blocks,
+                    blocks_per_head=blocks_per_head, d_r=d_r, page_size=page_size,
+                    max_pages_per_seq=max_pages_per_seq, num_pages=num_pages, d_model=d_model,
+                    dtype=dtype, softmax_scale=softmax_scale, out_scale=out_scale)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libmlra.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with compressed_kv_cache_mlra_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ip, dp = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MlraDesc)
+        L.mlra_abi_version.restype = ctypes.c_int
+        L.mlra_status_string.argtypes = [ctypes.c_int]
+        L.mlra_status_string.restype = ctypes.c_char_p
+        L.mlra_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+        L.mlra_workspace_bytes.restype = ctypes.c_size_t
+        L.mlra_append_latent.argtypes = [dp, vp, ip, ip, vp, vp, vp, vp, vp]
+        L.mlra_absorb_query.argtypes = [dp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mlra_attend.argtypes = [dp, vp, ip, vp, ctypes.c_size_t, vp]
+        L.mlra_decode.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
+        for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
+                  "mlra_combine", "mlra_read_flags"):
+            getattr(L, f).restype = ctypes.c_int
+        if L.mlra_abi_version() != ABI_VERSION:
+            raise ImportError("libmlra ABI version mismatch; rebuild the library")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mlra_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise MlraError(status, where)
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _elem_dtype(desc: MlraDesc):
+    torch = _torch()
+    return torch.bfloat16 if desc.dtype == BF16 else torch.float32
+
+
+def _ptr(t, desc: Optional[MlraDesc] = None, kind: str = "float", name: str = "tensor",
+         numel: Optional[int] = None, nullable: bool = False):
+    """Device pointer of a contiguous CUDA tensor, after checking dtype and size."""
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if kind == "float":
+        want = _elem_dtype(desc)
+        if t.dtype != want:
+            raise ValueError(f"{name} must be {want}, got {t.dtype}")
+    elif kind == "int32":
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32, got {t.dtype}")
+    elif kind == "f32":
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {t.dtype}")
+    elif kind == "bytes":
+        pass
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def workspace_bytes(desc: MlraDesc, max_seq_len: int) -> int:
+    n = lib().mlra_workspace_bytes(ctypes.byref(desc), int(max_seq_len))
+    if n == 0:
+        raise MlraError(ERR_INVALID_ARG, "workspace_bytes")
+    return int(n)
+
+
+def alloc_workspace(desc: MlraDesc, max_seq_len: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(workspace_bytes(desc, max_seq_len), dtype=torch.uint8, device=device)
+
+
+def _row(desc):
+    return desc.d_c + desc.d_r
+
+
+def _w(desc):
+    return desc.d_c // desc.n_blocks
+
+
+def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=None, stream=None):
+    B = desc.batch
+    _check(lib().mlra_append_latent(
+        ctypes.byref(desc),
+        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
+        _ptr(positions, kind="int32", name="positions", numel=B),
+        _ptr(x, desc, name="x", numel=B * desc.d_model),
+        _ptr(w_dkv, desc, name="w_dkv", numel=desc.d_model * desc.d_c),
+        _ptr(kr_new, desc, name="kr_new", numel=B * desc.d_r, nullable=desc.d_r == 0),
+        _ptr(c_out, desc, name="c_out", numel=B * desc.d_c, nullable=True),
+        _stream(stream)), "append_latent")
+
+
+def absorb_query(desc, seq_lens, q_c, q_r, w_uk, workspace, stream=None):
+    B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
+    _check(lib().mlra_absorb_query(
+        ctypes.byref(desc),
+        _ptr(seq_lens, kind="int32", name="seq_lens", numel=B),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=desc.d_r == 0),
+        _ptr(w_uk, desc, name="w_uk", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _stream(stream)), "absorb_query")
+
+
+def attend(desc, pool, page_table, workspace, stream=None):
+    _check(lib().mlra_attend(
+        ctypes.byref(desc),
+        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _ptr(page_table, kind="int32", name="page_table", numel=desc.batch * desc.max_pages_per_seq,
+             nullable=True),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _stream(stream)), "attend")
+
+
+def decode(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, workspace, stream=None):
+    B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
+    _check(lib().mlra_decode(
+        ctypes.byref(desc),
+        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
+        _ptr(seq_lens, kind="int32", name="seq_lens", numel=B), ctypes.c_int32(int(max_seq_len)),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=desc.d_r == 0),
+        _ptr(w_uk, desc, name="w_uk", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _stream(stream)), "decode")
+
+
+def combine(desc, workspace, w_uv, out, lse=None, stream=None):
+    B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
+    _check(lib().mlra_combine(
+        ctypes.byref(desc),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _ptr(w_uv, desc, name="w_uv", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(out, kind="f32", name="out", numel=B * H * desc.d_h),
+        _ptr(lse, kind="f32", name="lse", numel=B * H * K, nullable=True),
+        _stream(stream)), "combine")
+
+
+def read_flags(workspace, stream=None) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib().mlra_read_flags(_ptr(workspace, kind="bytes", name="workspace"),
+                                 ctypes.c_size_t(workspace.numel()), ctypes.byref(v), _stream(stream)),
+           "read_flags")
+    return int(v.value)
+
+
+@dataclasses.dataclass
+class DecodeStep:
+    """Convenience wrapper holding a descriptor and a workspace for repeated
+    decode steps: append (optional) -> absorb + attend -> combine."""
+    desc: MlraDesc
+    workspace: object
+    max_seq_len: int
+
+    @classmethod
+    def create(cls, desc: MlraDesc, max_seq_len: int, device="cuda"):
+        return cls(desc, alloc_workspace(desc, max_seq_len, device), int(max_seq_len))
+
+    def __call__(self, pool, page_table, seq_lens, q_c, q_r, w_uk, w_uv, out, lse=None, stream=None):
+        decode(self.desc, pool, page_table, seq_lens, self.max_seq_len, q_c, q_r, w_uk,
+               self.workspace, stream)
+        combine(self.desc, self.workspace, w_uv, out, lse, stream)
+        return out
+
+
+def default_softmax_scale(desc: MlraDesc) -> float:
+    return desc.softmax_scale if desc.softmax_scale > 0 else 1.0 / math.sqrt(desc.d_h + desc.d_r)

@@ -1,0 +1,249 @@
+// C ABI of libmlra: argument validation, work planning, workspace layout and
+// kernel launches. The public contract is documented in include/mlra.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mlra.h"
+#include "common.h"
+#include "launch.h"
+#include "validate.h"
+
+namespace mlra {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+struct Plan {
+  ShapeInfo s;
+  const MfmaVariant* variant;  // nullptr: generic path
+  int tile_tokens;
+  int groups;
+  int units;
+  int64_t slots;
+  size_t off_cum, off_nlen, off_qext, off_pm, off_pl, off_po, total;
+  bool q_bf16;
+};
+
+int make_plan(const mlra_desc* d, Plan* p) {
+  int st = check_desc(d, &p->s);
+  if (st != MLRA_OK) return st;
+  const ShapeInfo& s = p->s;
+  p->variant = d->dtype == MLRA_BF16 ? find_mfma_variant(s.w, d->d_r, d->n_blocks, s.head_tiles)
+                                     : nullptr;
+  if (p->variant) {
+    p->tile_tokens = p->variant->tile_tokens;
+    p->groups = p->variant->groups;
+    p->q_bf16 = true;
+  } else {
+    p->tile_tokens = kGenericTileTokens;
+    p->groups = 1;
+    p->q_bf16 = false;
+  }
+  p->units = compute_units();
+  p->slots = static_cast<int64_t>(p->units + d->batch) * p->groups;
+  const size_t qelem = p->q_bf16 ? 2 : 4;
+  size_t off = align_up(sizeof(WsHeader));
+  p->off_cum = off;
+  off = align_up(off + sizeof(int32_t) * (d->batch + 1));
+  p->off_nlen = off;
+  off = align_up(off + sizeof(int32_t) * d->batch);
+  p->off_qext = off;
+  off = align_up(off + qelem * static_cast<size_t>(d->batch) * s.hk * (s.w + d->d_r));
+  p->off_pm = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk);
+  p->off_pl = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk);
+  p->off_po = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk * s.w);
+  p->total = off;
+  return MLRA_OK;
+}
+
+DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, const int32_t* pt,
+                       void* ws) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pool = pool;
+  a.page_table = pt;
+  a.ws = static_cast<char*>(ws);
+  a.off_cum = static_cast<int64_t>(p.off_cum);
+  a.off_nlen = static_cast<int64_t>(p.off_nlen);
+  a.off_qext = static_cast<int64_t>(p.off_qext);
+  a.off_pm = static_cast<int64_t>(p.off_pm);
+  a.off_pl = static_cast<int64_t>(p.off_pl);
+  a.off_po = static_cast<int64_t>(p.off_po);
+  a.batch = d->batch;
+  a.n_heads = d->n_heads;
+  a.d_h = d->d_h;
+  a.w = p.s.w;
+  a.n_blocks = d->n_blocks;
+  a.k = d->blocks_per_head;
+  a.hpb = p.s.hpb;
+  a.d_r = d->d_r;
+  a.row = d->d_c + d->d_r;
+  a.page_size = d->page_size;
+  a.log2_page = p.s.log2_page;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.units = p.units;
+  a.tile_tokens = p.tile_tokens;
+  a.groups = p.groups;
+  const float sigma = d->softmax_scale > 0.f ? d->softmax_scale
+                                             : 1.0f / sqrtf(static_cast<float>(d->d_h + d->d_r));
+  a.qscale = sigma * 1.4426950408889634f;
+  a.out_scale = d->out_scale > 0.f ? d->out_scale
+                                   : 1.0f / sqrtf(static_cast<float>(d->blocks_per_head));
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLRA_OK : MLRA_ERR_HIP; }
+
+}  // namespace
+}  // namespace mlra
+
+using namespace mlra;
+
+extern "C" {
+
+int mlra_abi_version(void) { return 1; }
+
+const char* mlra_status_string(int status) {
+  switch (status) {
+    case MLRA_OK: return "ok";
+    case MLRA_ERR_INVALID_ARG: return "invalid argument";
+    case MLRA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLRA_ERR_WORKSPACE: return "workspace too small";
+    case MLRA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len) {
+  Plan p;
+  if (make_plan(desc, &p) != MLRA_OK) return 0;
+  if (max_seq_len < 0 || static_cast<int64_t>(max_seq_len) >
+                             static_cast<int64_t>(desc->max_pages_per_seq) * desc->page_size)
+    return 0;
+  return p.total;
+}
+
+int mlra_absorb_query(const mlra_desc* desc, const int32_t* seq_lens, const void* q_c,
+                      const void* q_r, const void* w_uk, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!seq_lens || !q_c || !w_uk || !workspace || (desc->d_r > 0 && !q_r)) return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(desc, p, nullptr, nullptr, workspace);
+  return hip_status(launch_absorb(a, desc->dtype, p.q_bf16, seq_lens, q_c, q_r, w_uk,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int mlra_attend(const mlra_desc* desc, const void* pool, const int32_t* page_table, void* workspace,
+                size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!pool || !workspace) return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(desc, p, pool, page_table, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.variant) return hip_status(launch_attend_mfma(p.variant, a, s));
+  return hip_status(launch_attend_generic(a, desc->dtype, s));
+}
+
+int mlra_decode(const mlra_desc* desc, const void* pool, const int32_t* page_table,
+                const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
+                const void* w_uk, void* workspace, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!pool || !seq_lens || !q_c || !w_uk || !workspace || (desc->d_r > 0 && !q_r))
+    return MLRA_ERR_INVALID_ARG;
+  if (max_seq_len < 0 || static_cast<int64_t>(max_seq_len) >
+                             static_cast<int64_t>(desc->max_pages_per_seq) * desc->page_size)
+    return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  st = mlra_absorb_query(desc, seq_lens, q_c, q_r, w_uk, workspace, ws_bytes, stream);
+  if (st != MLRA_OK) return st;
+  return mlra_attend(desc, pool, page_table, workspace, ws_bytes, stream);
+}
+
+int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, const void* w_uv,
+                 float* out, float* lse, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!workspace || !w_uv || !out) return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.ws = static_cast<const char*>(workspace);
+  c.w_uv = w_uv;
+  c.out = out;
+  c.lse = lse;
+  c.off_cum = static_cast<int64_t>(p.off_cum);
+  c.off_pm = static_cast<int64_t>(p.off_pm);
+  c.off_pl = static_cast<int64_t>(p.off_pl);
+  c.off_po = static_cast<int64_t>(p.off_po);
+  c.batch = desc->batch;
+  c.n_heads = desc->n_heads;
+  c.d_h = desc->d_h;
+  c.w = p.s.w;
+  c.k = desc->blocks_per_head;
+  c.hk = p.s.hk;
+  c.out_scale = desc->out_scale > 0.f ? desc->out_scale
+                                      : 1.0f / sqrtf(static_cast<float>(desc->blocks_per_head));
+  return hip_status(launch_combine(c, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
+int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,
+                       const int32_t* positions, const void* x, const void* w_dkv,
+                       const void* kr_new, void* c_out, void* stream) {
+  ShapeInfo s;
+  int st = check_desc(desc, &s);
+  if (st != MLRA_OK) return st;
+  st = check_append(desc);
+  if (st != MLRA_OK) return st;
+  if (!pool || !positions || !x || !w_dkv || (desc->d_r > 0 && !kr_new)) return MLRA_ERR_INVALID_ARG;
+  AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pool = pool;
+  a.page_table = page_table;
+  a.positions = positions;
+  a.x = x;
+  a.w_dkv = w_dkv;
+  a.kr_new = kr_new;
+  a.c_out = c_out;
+  a.batch = desc->batch;
+  a.d_c = desc->d_c;
+  a.d_r = desc->d_r;
+  a.d_model = desc->d_model;
+  a.row = desc->d_c + desc->d_r;
+  a.page_size = desc->page_size;
+  a.max_pages = desc->max_pages_per_seq;
+  a.num_pages = desc->num_pages;
+  return hip_status(launch_append(a, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
+int mlra_read_flags(const void* workspace, size_t ws_bytes, uint32_t* flags, void* stream) {
+  if (!workspace || !flags || ws_bytes < sizeof(WsHeader)) return MLRA_ERR_INVALID_ARG;
+  const WsHeader* h = static_cast<const WsHeader*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(flags, &h->flags, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MLRA_ERR_HIP;
+  return hip_status(hipStreamSynchronize(s));
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Shared definitions of libmlra's kernels and host layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlra {
+
+// Workspace layout (all offsets 256-byte aligned):
+//   [0, 256)     WsHeader
+//   cum          int32 [batch + 1]  prefix sums of tiles per sequence
+//   nlen         int32 [batch]      clamped sequence lengths
+//   qext         [batch][hk][w + d_r]  absorbed queries (bf16 or fp32), base-2 scaled
+//   pm, pl       fp32 [slots][hk]      partial running max / sum
+//   po           fp32 [slots][hk][w]   partial weighted latent sums
+// hk = n_heads * blocks_per_head; slots = (units + batch) * groups.
+struct WsHeader {
+  uint32_t magic;
+  uint32_t flags;
+  int32_t n_tiles;
+  int32_t units;
+  int32_t tile_tokens;
+  int32_t groups;
+  int32_t batch;
+  int32_t hk;
+  int32_t pad[56];
+};
+static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+
+constexpr uint32_t kWsMagic = 0x4d4c5241u;  // "MLRA"
+constexpr uint32_t kFlagBadPage = 1u;       // same value as MLRA_FLAG_BAD_PAGE
+
+// Everything a decode kernel needs, passed by value.
+struct DecodeArgs {
+  const void* pool;
+  const int32_t* page_table;  // nullptr: identity layout
+  char* ws;
+  int64_t off_cum, off_nlen, off_qext, off_pm, off_pl, off_po;
+  int32_t batch;
+  int32_t n_heads;
+  int32_t d_h;
+  int32_t w;          // latent block width
+  int32_t n_blocks;   // blocks per cache row
+  int32_t k;          // blocks per head
+  int32_t hpb;        // heads per block (h k / b)
+  int32_t d_r;
+  int32_t row;        // elements per cache row (n_blocks * w + d_r)
+  int32_t page_size;
+  int32_t log2_page;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t units;
+  int32_t tile_tokens;
+  int32_t groups;
+  float qscale;       // softmax_scale * log2(e)
+  float out_scale;
+};
+
+struct AppendArgs {
+  void* pool;
+  const int32_t* page_table;
+  const int32_t* positions;
+  const void* x;
+  const void* w_dkv;
+  const void* kr_new;
+  void* c_out;
+  int32_t batch, d_c, d_r, d_model, row, page_size, max_pages, num_pages;
+};
+
+struct CombineArgs {
+  const char* ws;
+  const void* w_uv;
+  float* out;
+  float* lse;
+  int64_t off_cum, off_pm, off_pl, off_po;
+  int32_t batch, n_heads, d_h, w, k, hk;
+  float out_scale;
+};
+
+// ------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ T store_cast(float v);
+template <>
+__device__ __forceinline__ float store_cast<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t store_cast<uint16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work split: the concatenated tiles of all sequences are cut into `units`
+// contiguous ranges of near-equal length; unit u owns [tile_begin(u), tile_begin(u+1)).
+__device__ __forceinline__ int32_t tile_begin(int32_t u, int32_t n_tiles, int32_t units) {
+  return static_cast<int32_t>((static_cast<int64_t>(u) * n_tiles) / units);
+}
+__device__ __forceinline__ bool unit_owns_tiles(int32_t u, int32_t n_tiles, int32_t units) {
+  return tile_begin(u + 1, n_tiles, units) > tile_begin(u, n_tiles, units);
+}
+// The unit whose range contains tile x (largest u with tile_begin(u) <= x).
+__device__ __forceinline__ int32_t unit_of_tile(int32_t x, int32_t n_tiles, int32_t units) {
+  return static_cast<int32_t>(((static_cast<int64_t>(x) + 1) * units - 1) / n_tiles);
+}
+
+}  // namespace mlra

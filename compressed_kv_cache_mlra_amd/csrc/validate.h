@@ -1,0 +1,23 @@
+// Host-side descriptor validation of libmlra (no HIP calls: runs before any
+// launch, and on machines without a GPU).
+#pragma once
+
+#include "../../include/mlra.h"
+
+namespace mlra {
+
+struct ShapeInfo {
+  int w;           // latent block width d_c / n_blocks
+  int hpb;         // heads per block h k / b
+  int head_tiles;  // ceil(hpb / 16)
+  int hk;          // head-block pairs h k
+  int log2_page;
+};
+
+// Checks a descriptor; fills `s` on success. Returns an mlra_status.
+int check_desc(const mlra_desc* d, ShapeInfo* s);
+
+// Extra checks of the append entry point.
+int check_append(const mlra_desc* d);
+
+}  // namespace mlra

@@ -1,0 +1,164 @@
+/*
+ * mlra.h: C ABI of libmlra, MLRA decode attention over a paged latent cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method (sources are the pages this library follows):
+ *  - The cache keeps, per token, the compressed latent c = W^DKV x and a
+ *    d_r-wide RoPE key k^R shared by all heads ("Multi-Head Latent Attention
+ *    (MLA): How Low-Rank KV Compression Crushes Transformer Memory Footprints
+ *    by 93%", lesty.tech, sections 3 and 4; "Multi-Head Latent Attention",
+ *    ai360xpert, "The two projections").
+ *  - MLRA splits the latent into n_blocks independent latent heads, each
+ *    serving a subset of the query heads; per-subset results are combined
+ *    ("Multi-Head Low-Rank Attention: Making Compressed Attention Actually
+ *    Parallelizable", alanhou.org, "Core Mechanism"). With blocks_per_head > 1
+ *    a head attends several blocks with separate softmaxes and the outputs are
+ *    summed times out_scale (the alpha_attn of Tables 16 and 17 on the
+ *    "Multi-Head Low-Rank Attention" paper page, thelatestinai.com).
+ *  - The up-projections are absorbed: the query is mapped into latent space
+ *    once, scores are dot products with the raw cached latent, and W^UV is
+ *    applied once to the softmax-weighted latent sum (lesty.tech, section 5).
+ *
+ * Notation: h = n_heads query heads of width d_h; latent width d_c per cache
+ * row cut into b = n_blocks blocks of width w = d_c / b; k = blocks_per_head;
+ * head i belongs to group g = i / (h k / b) and attends blocks g k + jj,
+ * jj = 0 .. k-1. The softmax scale defaults to 1 / sqrt(d_h + d_r).
+ *
+ * Memory and ownership (every entry point):
+ *  - Every pointer argument is a caller-owned DEVICE pointer (except `desc`,
+ *    which is host memory read during the call). Arrays are dense, row-major,
+ *    16-byte aligned. The library allocates nothing and keeps no state across
+ *    calls; it is safe to call from several host threads on different streams
+ *    with different workspaces.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All work is
+ *    enqueued on it asynchronously; results are ready when the stream is.
+ *  - Element type: every floating-point input (pool, queries, weights, x,
+ *    k^R_new, c_out) uses desc->dtype; outputs `out` and `lse` are fp32.
+ *
+ * Cache layout (all entry points):
+ *  - pool: [num_pages][page_size][d_c + d_r]; row = [c (d_c) | k^R (d_r)].
+ *  - page_table: int32 [batch][max_pages_per_seq]; token t of sequence b lives
+ *    in row page_table[b][t / page_size] * page_size + t % page_size.
+ *    NULL means the identity layout: page p of sequence b is
+ *    b * max_pages_per_seq + p.
+ *  - Only page-table entries for pages that hold tokens are read. A page id
+ *    outside [0, num_pages) is never dereferenced: that page is read as page 0
+ *    instead and the error flag MLRA_FLAG_BAD_PAGE is raised in the workspace.
+ *
+ * Errors: every entry point validates its arguments on the host before
+ * enqueuing anything. On failure it returns a negative mlra_status and touches
+ * no buffer. A failed launch returns MLRA_ERR_HIP. Faults during execution
+ * surface at the caller's next synchronisation, as usual for HIP.
+ */
+#ifndef MLRA_H
+#define MLRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLRA_OK = 0,
+  MLRA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape */
+  MLRA_ERR_UNSUPPORTED = -2, /* a shape or dtype this build has no kernel for */
+  MLRA_ERR_WORKSPACE = -3,   /* workspace smaller than mlra_workspace_bytes() */
+  MLRA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} mlra_status;
+
+typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1 } mlra_dtype;
+
+/* Error flags a kernel can raise in the workspace (see mlra_read_flags). */
+#define MLRA_FLAG_BAD_PAGE 1u
+
+typedef struct {
+  int32_t batch;             /* B, number of sequences (>= 1) */
+  int32_t n_heads;           /* h */
+  int32_t d_h;               /* query / value head width (1 .. 512) */
+  int32_t d_c;               /* latent width stored in each cache row */
+  int32_t n_blocks;          /* b: latent blocks per row (1 = MLA); divides d_c */
+  int32_t blocks_per_head;   /* k: blocks each head attends (divides b) */
+  int32_t d_r;               /* RoPE key width (0 .. 512) */
+  int32_t page_size;         /* tokens per page: power of two in [16, 256] */
+  int32_t max_pages_per_seq; /* page-table row length */
+  int32_t num_pages;         /* pages in the pool */
+  int32_t d_model;           /* append only: width of x */
+  int32_t dtype;             /* mlra_dtype */
+  float softmax_scale;       /* <= 0 selects 1 / sqrt(d_h + d_r) */
+  float out_scale;           /* <= 0 selects 1 / sqrt(blocks_per_head) */
+} mlra_desc;
+
+/* Bytes of device workspace mlra_decode / mlra_combine need for this shape.
+ * Depends on the shape and on the number of compute units of the current
+ * device, not on the sequence lengths. Returns 0 for an invalid descriptor.
+ * max_seq_len: upper bound of the lengths the workspace will be used with
+ * (validated to be >= 0 and <= max_pages_per_seq * page_size). */
+size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len);
+
+/* Latent append (the down-projection c = W^DKV x of ai360xpert, "The two
+ * projections"; W^DKV stored [d_model][d_c]):
+ *   c_new[b] = x[b] W^DKV, accumulated in fp32 and rounded once to dtype
+ *   (round to nearest, ties to even), then the row [c_new[b] | kr_new[b]] is
+ *   written to the pool slot of token positions[b] of sequence b.
+ *   x: [batch][d_model]; w_dkv: [d_model][d_c]; kr_new: [batch][d_r] (already
+ *   rotated); positions: int32 [batch] (device); c_out: [batch][d_c] or NULL.
+ * A position outside [0, max_pages_per_seq * page_size) writes nothing. The
+ * caller advances its sequence lengths itself. */
+int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,
+                       const int32_t* positions, const void* x, const void* w_dkv,
+                       const void* kr_new, void* c_out, void* stream);
+
+/* Query absorption (lesty.tech section 5; ai360xpert "Absorbing the
+ * up-projection") and work planning:
+ *   q~[b][i][jj] = s * W^UK[i][jj]^T q_c[b][i],  q^R~[b][i] = s * q_r[b][i],
+ *   s = softmax_scale * log2(e) (scores are then base-2 logits),
+ * written into the workspace, plus the split of all sequences' tokens into
+ * balanced work units, computed on the device from seq_lens.
+ *   q_c: [batch][h][d_h]; q_r: [batch][h][d_r]; w_uk: [h][k][w][d_h];
+ *   seq_lens: int32 [batch] (device), lengths the decode attends; values above
+ *   max_pages_per_seq * page_size are clamped to it, negative values read as 0. */
+int mlra_absorb_query(const mlra_desc* desc, const int32_t* seq_lens, const void* q_c,
+                      const void* q_r, const void* w_uk, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Split-K latent attention over the paged cache (the kernel that streams the
+ * cache; lesty.tech section 6 describes the MLA analogue): for every work unit
+ * and every (head, attended block), base-2 scores q~ . c_j + q^R~ . k^R,
+ * online max and sum, and the weighted latent sum sum_t 2^(l_t - m) c_{t,j},
+ * written as (m, l, o~) partials into the workspace. Needs the workspace
+ * filled by mlra_absorb_query for the same descriptor. */
+int mlra_attend(const mlra_desc* desc, const void* pool, const int32_t* page_table, void* workspace,
+                size_t ws_bytes, void* stream);
+
+/* mlra_absorb_query followed by mlra_attend. */
+int mlra_decode(const mlra_desc* desc, const void* pool, const int32_t* page_table,
+                const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
+                const void* w_uk, void* workspace, size_t ws_bytes, void* stream);
+
+/* Log-sum-exp merge of the partials of each sequence and the absorbed value
+ * up-projection (lesty.tech section 5; "results get combined", alanhou.org
+ * "Core Mechanism"):
+ *   o~[b][i][jj] = merged softmax-weighted latent sum of block J(i)[jj];
+ *   out[b][i] = out_scale * sum_jj W^UV[i][jj]^T o~[b][i][jj]   (fp32 [batch][h][d_h])
+ *   lse[b][i][jj] = natural-log log-sum-exp of the scaled logits (fp32
+ *   [batch][h][k]; NULL to skip). An empty sequence gives out = 0, lse = -inf.
+ *   w_uv: [h][k][w][d_h]. */
+int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, const void* w_uv,
+                 float* out, float* lse, void* stream);
+
+/* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host) and
+ * clears them. Synchronises `stream`. */
+int mlra_read_flags(const void* workspace, size_t ws_bytes, uint32_t* flags, void* stream);
+
+/* Text for a status code. Never NULL. */
+const char* mlra_status_string(int status);
+
+/* ABI version: bumped when a signature or the descriptor changes. */
+int mlra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLRA_H */

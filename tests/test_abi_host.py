@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_kv_cache_mlra_amd as mlra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlra.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlra_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mlra.lib()
+    names = _declared_symbols()
+    assert {"mlra_append_latent", "mlra_decode", "mlra_combine"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert mlra.lib().mlra_abi_version() == mlra.ABI_VERSION
+    for code in (0, -1, -2, -3, -4):
+        assert mlra.status_string(code) != "unknown status"
+    assert mlra.status_string(7) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(batch=2, n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16, max_pages_per_seq=4,
+                num_pages=8, dtype="f32", page_size=64)
+    base.update(kw)
+    return mlra.make_desc(**base)
+
+
+def _decode(desc, ws_bytes=1 << 30, pool=FAKE, seq_lens=FAKE, q_c=FAKE, q_r=FAKE, w_uk=FAKE,
+            ws=FAKE, max_seq_len=10):
+    return mlra.lib().mlra_decode(ctypes.byref(desc), pool, None, seq_lens, max_seq_len, q_c, q_r,
+                                  w_uk, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+BAD_DESCS = [
+    (dict(batch=0), mlra.ERR_INVALID_ARG),
+    (dict(n_heads=0), mlra.ERR_INVALID_ARG),
+    (dict(d_c=66), mlra.ERR_INVALID_ARG),            # d_c not divisible by n_blocks
+    (dict(n_heads=6), mlra.ERR_INVALID_ARG),         # h not divisible by b / k
+    (dict(blocks_per_head=3), mlra.ERR_INVALID_ARG),  # k does not divide b
+    (dict(page_size=48), mlra.ERR_INVALID_ARG),      # not a power of two
+    (dict(page_size=8), mlra.ERR_INVALID_ARG),
+    (dict(page_size=512), mlra.ERR_INVALID_ARG),
+    (dict(d_r=2), mlra.ERR_INVALID_ARG),             # row bytes not a multiple of 16
+    (dict(dtype="bf16", d_c=4 * 12, d_r=16), mlra.ERR_INVALID_ARG),  # bf16 block width % 8
+    (dict(dtype=7), mlra.ERR_UNSUPPORTED),
+    (dict(d_h=1024), mlra.ERR_UNSUPPORTED),
+    (dict(d_c=4 * 1024), mlra.ERR_UNSUPPORTED),      # block wider than 512
+    (dict(max_pages_per_seq=0), mlra.ERR_INVALID_ARG),
+    (dict(num_pages=0), mlra.ERR_INVALID_ARG),
+    (dict(d_r=-8), mlra.ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), mlra.ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DESCS)
+def test_bad_descriptor(kw, code):
+    if kw.get("dtype") == 7:
+        d = _desc()
+        d.dtype = 7
+    else:
+        d = _desc(**kw)
+    assert _decode(d) == code
+    assert mlra.lib().mlra_workspace_bytes(ctypes.byref(d), 10) == 0
+
+
+def test_null_descriptor():
+    L = mlra.lib()
+    assert L.mlra_decode(None, FAKE, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == mlra.ERR_INVALID_ARG
+    assert L.mlra_workspace_bytes(None, 1) == 0
+
+
+@pytest.mark.parametrize("field", ["pool", "seq_lens", "q_c", "q_r", "w_uk", "ws"])
+def test_null_pointers(field):
+    d = _desc()
+    assert _decode(d, **{field: None}) == mlra.ERR_INVALID_ARG
+
+
+def test_max_seq_len_range():
+    d = _desc()
+    assert _decode(d, max_seq_len=-1) == mlra.ERR_INVALID_ARG
+    assert _decode(d, max_seq_len=4 * 64 + 1) == mlra.ERR_INVALID_ARG
+    assert mlra.lib().mlra_workspace_bytes(ctypes.byref(d), 4 * 64 + 1) == 0
+
+
+def test_workspace_too_small():
+    d = _desc()
+    need = mlra.workspace_bytes(d, 100)
+    assert need > 0
+    assert _decode(d, ws_bytes=need - 1) == mlra.ERR_WORKSPACE
+    L = mlra.lib()
+    assert L.mlra_combine(ctypes.byref(d), FAKE, ctypes.c_size_t(need - 1), FAKE, FAKE, None, None) == \
+        mlra.ERR_WORKSPACE
+    assert L.mlra_attend(ctypes.byref(d), FAKE, None, FAKE, ctypes.c_size_t(need - 1), None) == \
+        mlra.ERR_WORKSPACE
+
+
+def test_workspace_independent_of_lengths():
+    d = _desc()
+    assert mlra.workspace_bytes(d, 0) == mlra.workspace_bytes(d, 256)
+
+
+def test_combine_and_append_validation():
+    L = mlra.lib()
+    d = _desc()
+    assert L.mlra_combine(ctypes.byref(d), None, 1 << 30, FAKE, FAKE, None, None) == mlra.ERR_INVALID_ARG
+    assert L.mlra_combine(ctypes.byref(d), FAKE, 1 << 30, FAKE, None, None, None) == mlra.ERR_INVALID_ARG
+    # append needs d_model >= 1
+    assert L.mlra_append_latent(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        mlra.ERR_INVALID_ARG
+    d2 = _desc(d_model=32)
+    assert L.mlra_append_latent(ctypes.byref(d2), None, None, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        mlra.ERR_INVALID_ARG
+    assert L.mlra_append_latent(ctypes.byref(d2), FAKE, None, FAKE, FAKE, FAKE, None, None, None) == \
+        mlra.ERR_INVALID_ARG  # k^R_new required when d_r > 0
+
+
+def test_read_flags_validation():
+    v = ctypes.c_uint32(0)
+    assert mlra.lib().mlra_read_flags(None, 256, ctypes.byref(v), None) == mlra.ERR_INVALID_ARG
+    assert mlra.lib().mlra_read_flags(FAKE, 16, ctypes.byref(v), None) == mlra.ERR_INVALID_ARG
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    d = _desc()
+    with pytest.raises(ValueError):
+        mlra.attend(d, torch.zeros(10), None, torch.zeros(10, dtype=torch.uint8))
