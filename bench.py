@@ -1,0 +1,229 @@
+"""Decode-step benchmark of libmlra on one MI355X.
+
+A step is one pass of the whole decode path over one batch: query absorption,
+split-K latent attention over the paged cache, log-sum-exp combine with the
+value up-projection (plus the latent append for the ragged workload). Inputs are
+seeded synthetic data with the workload's shapes, resident in HBM before timing.
+Several independent cache pools are rotated so the 256 MB Infinity Cache cannot
+serve the cache stream.
+
+Prints one JSON line. `value` is decode tokens/s (batch / step time). The
+`roofline` object reports the attention kernel (the one that streams the cache):
+algorithmic cache bytes per launch / its mean duration from HIP events recorded
+around every launch on the launch stream inside the timed region, against the
+8 TB/s HBM3E peak. `cpu_baseline` times the CPU oracle (test infrastructure, used
+here only for this baseline) on a bounded sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8K, 1 GPU"
+KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_mfma_mlra4_b32_ctx8k_counters.txt")
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def _source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(bytes_alg: float):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter summary, when it was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != _source_hash():
+        return None
+    f = re.search(r"hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    w = re.search(r"hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not f or not w:
+        return None
+    return {"read_bytes": float(f.group(1)), "write_bytes": float(w.group(1)),
+            "algorithmic_bytes": bytes_alg,
+            "read_over_algorithmic": float(f.group(1)) / bytes_alg}
+
+
+def main():
+    args = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the decode path "
+              "has no multi-GPU component; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_kv_cache_mlra_amd as mlra
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.workload_inputs(args.workload, pool_copies=args.pools)
+    pools_np = inp.pool if isinstance(inp.pool, list) else [inp.pool]
+    s = inp.shape
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.to("cuda")
+
+    pools = [dev(p) for p in pools_np]
+    page_table = None if inp.page_table is None else dev(inp.page_table)
+    seq_lens, q_c, q_r = dev(inp.seq_lens), dev(inp.q_c), dev(inp.q_r)
+    w_uk, w_uv = dev(inp.w_uk), dev(inp.w_uv)
+    append = inp.x is not None
+    if append:
+        positions, x, w_dkv, kr_new = dev(inp.positions), dev(inp.x), dev(inp.w_dkv), dev(inp.kr_new)
+    desc = mlra.make_desc(batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
+                          d_r=s.d_r, max_pages_per_seq=inp.max_pages_per_seq,
+                          num_pages=pools_np[0].shape[0], dtype=s.dtype, page_size=s.page_size,
+                          blocks_per_head=s.blocks_per_head, d_model=s.d_model)
+    ws = mlra.alloc_workspace(desc, inp.max_seq_len)
+    out = torch.empty((s.batch, s.n_heads, s.d_h), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    setup_s = time.time() - t0
+
+    def step(i, ev=None):
+        pool = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        if append:
+            mlra.append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, None, stream)
+        mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mlra.attend(desc, pool, page_table, ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        mlra.combine(desc, ws, w_uv, out, None, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attend_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+
+    elem = 2 if s.dtype == "bf16" else 4
+    n_tokens = int(np.sum(inp.seq_lens.astype(np.int64)))
+    cache_bytes = float(n_tokens) * (s.d_c + s.d_r) * elem  # read once per step, k^R not re-read
+    heads_per_block = s.n_heads * s.blocks_per_head // s.n_blocks
+    # per token: every (head, attended block) pair scores w + d_r and accumulates w
+    attn_flops = float(n_tokens) * s.n_heads * s.blocks_per_head * (4.0 * s.w + 2.0 * s.d_r)
+    attend_mean_ms = float(np.mean(attend_ms))
+    achieved = cache_bytes / (attend_mean_ms * 1e-3) / 1e9
+    tokens_per_s = s.batch / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "batch": s.batch, "n_heads": s.n_heads, "d_h": s.d_h,
+                   "d_c": s.d_c, "n_blocks": s.n_blocks, "d_r": s.d_r, "page_size": s.page_size,
+                   "context_tokens": n_tokens, "heads_per_block": heads_per_block,
+                   "pool_instances": len(pools), "parallelism": "single GPU"},
+        "cache_gbps_full_step": round(cache_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "cache_pct_of_hbm_peak_full_step": round(100.0 * cache_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "kernel_us": {"append_absorb": round(1e3 * float(np.mean(pre_ms)), 2),
+                      "attend": round(1e3 * attend_mean_ms, 2),
+                      "attend_p10": round(1e3 * float(np.percentile(attend_ms, 10)), 2),
+                      "attend_p90": round(1e3 * float(np.percentile(attend_ms, 90)), 2),
+                      "combine": round(1e3 * float(np.mean(comb_ms)), 2)},
+        "roofline": {
+            "kernel": "attend_mfma_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes_per_launch": cache_bytes,
+            "traffic": _traffic(cache_bytes),
+            "mfma_tflops": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12, 2),
+            "mfma_frac_of_bf16_peak": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        },
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _cpu_baseline(inp, target_s: float):
+    """The oracle, as it stands, on whole sequences of the same workload (all
+    heads of sequence 0, then 1, ...) until about target_s seconds of work."""
+    import oracle
+
+    s = inp.shape
+    pool = inp.pool[0] if isinstance(inp.pool, list) else inp.pool
+    done, spent = 0, 0.0
+    order = list(range(s.batch))
+    while done < len(order) and spent < target_s:
+        b = order[done]
+        t = time.perf_counter()
+        oracle.decode_unabsorbed(inp, [(b, i) for i in range(s.n_heads)], pool=pool)
+        spent += time.perf_counter() - t
+        done += 1
+    tokens = sum(int(inp.seq_lens[b]) for b in order[:done])
+    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {s.batch} sequences, all {s.n_heads} heads each "
+                      f"({tokens} cached tokens), un-absorbed fp64 oracle, {spent:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

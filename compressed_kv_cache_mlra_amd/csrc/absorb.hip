@@ -15,6 +15,50 @@ namespace {
 constexpr int kAbsorbThreads = 256;
 constexpr int kAbsorbBatchGroup = 8;
 
+// Work plan, written by one workgroup: clamped lengths, tiles per sequence
+// and their exclusive prefix sum, and the workspace header.
+__device__ void write_plan(const DecodeArgs& a, const int32_t* seq_lens) {
+  __shared__ int32_t scan_sh[kAbsorbThreads];
+  const int tid = threadIdx.x;
+  int32_t* cum = reinterpret_cast<int32_t*>(a.ws + a.off_cum);
+  int32_t* nlen = reinterpret_cast<int32_t*>(a.ws + a.off_nlen);
+  const int32_t cap = a.max_pages * a.page_size;
+  int32_t carry = 0;
+  for (int base = 0; base < a.batch; base += kAbsorbThreads) {
+    const int b = base + tid;
+    int32_t tiles = 0;
+    if (b < a.batch) {
+      int32_t n = seq_lens[b];
+      n = n < 0 ? 0 : (n > cap ? cap : n);
+      nlen[b] = n;
+      tiles = (n + a.tile_tokens - 1) / a.tile_tokens;
+    }
+    scan_sh[tid] = tiles;
+    __syncthreads();
+    for (int off = 1; off < kAbsorbThreads; off <<= 1) {
+      const int32_t v = tid >= off ? scan_sh[tid - off] : 0;
+      __syncthreads();
+      scan_sh[tid] += v;
+      __syncthreads();
+    }
+    if (b < a.batch) cum[b] = carry + scan_sh[tid] - tiles;
+    carry += scan_sh[kAbsorbThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    cum[a.batch] = carry;
+    WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);
+    h->magic = kWsMagic;
+    h->flags = 0;
+    h->n_tiles = carry;
+    h->units = a.units;
+    h->tile_tokens = a.tile_tokens;
+    h->groups = a.groups;
+    h->batch = a.batch;
+    h->hk = a.n_heads * a.k;
+  }
+}
+
 // grid: (hk, ceil(batch / kAbsorbBatchGroup)); block: kAbsorbThreads.
 // Block (0, 0) also writes the work plan into the workspace header.
 template <typename TIn, typename TQ>
@@ -23,7 +67,6 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
                                                                  const TIn* __restrict__ q_r,
                                                                  const TIn* __restrict__ w_uk) {
   extern __shared__ float q_sh[];  // [kAbsorbBatchGroup][d_h]
-  __shared__ int32_t scan_sh[kAbsorbThreads];
   const int tid = threadIdx.x;
   const int hk = blockIdx.x;
   const int head = hk / a.k;
@@ -32,46 +75,7 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
   const int HK = a.n_heads * a.k;
   const int QW = a.w + a.d_r;
 
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    // Plan: clamp lengths, count tiles per sequence, exclusive prefix sum.
-    int32_t* cum = reinterpret_cast<int32_t*>(a.ws + a.off_cum);
-    int32_t* nlen = reinterpret_cast<int32_t*>(a.ws + a.off_nlen);
-    const int32_t cap = a.max_pages * a.page_size;
-    int32_t carry = 0;
-    for (int base = 0; base < a.batch; base += kAbsorbThreads) {
-      const int b = base + tid;
-      int32_t tiles = 0;
-      if (b < a.batch) {
-        int32_t n = seq_lens[b];
-        n = n < 0 ? 0 : (n > cap ? cap : n);
-        nlen[b] = n;
-        tiles = (n + a.tile_tokens - 1) / a.tile_tokens;
-      }
-      scan_sh[tid] = tiles;
-      __syncthreads();
-      for (int off = 1; off < kAbsorbThreads; off <<= 1) {
-        const int32_t v = tid >= off ? scan_sh[tid - off] : 0;
-        __syncthreads();
-        scan_sh[tid] += v;
-        __syncthreads();
-      }
-      if (b < a.batch) cum[b] = carry + scan_sh[tid] - tiles;
-      carry += scan_sh[kAbsorbThreads - 1];
-      __syncthreads();
-    }
-    if (tid == 0) {
-      cum[a.batch] = carry;
-      WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);
-      h->magic = kWsMagic;
-      h->flags = 0;
-      h->n_tiles = carry;
-      h->units = a.units;
-      h->tile_tokens = a.tile_tokens;
-      h->groups = a.groups;
-      h->batch = a.batch;
-      h->hk = HK;
-    }
-  }
+  if (blockIdx.x == 0 && blockIdx.y == 0) write_plan(a, seq_lens);
 
   for (int e = tid; e < nb * a.d_h; e += kAbsorbThreads) {
     const int bl = e / a.d_h, d = e % a.d_h;
@@ -104,6 +108,64 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 absorption on MFMA: for head-block pair hk and a 16-sequence tile,
+//   D[c][b] = sum_d W^UK[hk][c][d] q^C[b][head][d]   (v_mfma_f32_16x16x32_bf16)
+// with W^UK rows as the A operand and queries as the B operand, both read
+// straight from global memory 16 bytes per lane. grid: (hk, ceil(batch / 16)).
+__global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs a, const int32_t* seq_lens,
+                                                                      const uint16_t* __restrict__ q_c,
+                                                                      const uint16_t* __restrict__ q_r,
+                                                                      const uint16_t* __restrict__ w_uk) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hk = blockIdx.x;
+  const int head = hk / a.k;
+  const int b0 = blockIdx.y * 16;
+  const int HK = a.n_heads * a.k;
+  const int QW = a.w + a.d_r;
+  if (blockIdx.x == 0 && blockIdx.y == 0) write_plan(a, seq_lens);
+
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int b = b0 + m16;
+  const bool b_ok = b < a.batch;
+  const uint16_t* qrow = q_c + (static_cast<int64_t>(b) * a.n_heads + head) * a.d_h;
+  const uint16_t* wbase = w_uk + static_cast<int64_t>(hk) * a.w * a.d_h;
+  uint16_t* qext = reinterpret_cast<uint16_t*>(a.ws + a.off_qext);
+  const int n_mt = a.w / 16;
+  for (int mt = wave; mt < n_mt; mt += kAbsorbThreads / 64) {
+    floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* wrow = wbase + static_cast<int64_t>(mt * 16 + m16) * a.d_h;
+    for (int d0 = 0; d0 < a.d_h; d0 += 32) {
+      const int d = d0 + 8 * g4;
+      u32x4_t av = u32x4_t{0u, 0u, 0u, 0u}, bv = av;
+      if (d < a.d_h) {
+        av = *reinterpret_cast<const u32x4_t*>(wrow + d);
+        if (b_ok) bv = *reinterpret_cast<const u32x4_t*>(qrow + d);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+    }
+    if (b_ok) {
+      // lane holds rows c = mt*16 + 4 g4 + i of sequence b: 4 consecutive outputs
+      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[0] * a.qscale)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[1] * a.qscale)) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[2] * a.qscale)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[3] * a.qscale)) << 16);
+      uint2* dst = reinterpret_cast<uint2*>(qext + (static_cast<int64_t>(b) * HK + hk) * QW + mt * 16 + 4 * g4);
+      *dst = make_uint2(lo, hi);
+    }
+  }
+  const int nb = min(16, a.batch - b0);
+  for (int e = tid; e < nb * a.d_r; e += kAbsorbThreads) {
+    const int bl = e / a.d_r, r = e % a.d_r;
+    const float v = bf16_to_f32(q_r[(static_cast<int64_t>(b0 + bl) * a.n_heads + head) * a.d_r + r]);
+    qext[(static_cast<int64_t>(b0 + bl) * HK + hk) * QW + a.w + r] = f32_to_bf16(v * a.qscale);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int32_t* seq_lens,
@@ -111,7 +173,11 @@ hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int3
   const dim3 grid(a.n_heads * a.k, (a.batch + kAbsorbBatchGroup - 1) / kAbsorbBatchGroup);
   const size_t sh = sizeof(float) * kAbsorbBatchGroup * a.d_h;
   if (dtype == 1) {
-    if (q_bf16)
+    if (q_bf16 && a.d_h % 8 == 0 && a.w % 16 == 0)
+      absorb_mfma_kernel<<<dim3(a.n_heads * a.k, (a.batch + 15) / 16), kAbsorbThreads, 0, stream>>>(
+          a, seq_lens, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
+          static_cast<const uint16_t*>(w_uk));
+    else if (q_bf16)
       absorb_kernel<uint16_t, uint16_t><<<grid, kAbsorbThreads, sh, stream>>>(
           a, seq_lens, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
           static_cast<const uint16_t*>(w_uk));

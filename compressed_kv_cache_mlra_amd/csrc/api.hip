@@ -49,7 +49,7 @@ int make_plan(const mlra_desc* d, Plan* p) {
     p->groups = 1;
     p->q_bf16 = false;
   }
-  p->units = compute_units();
+  p->units = compute_units() * (p->variant ? p->variant->occupancy : 1);
   p->slots = static_cast<int64_t>(p->units + d->batch) * p->groups;
   const size_t qelem = p->q_bf16 ? 2 : 4;
   size_t off = align_up(sizeof(WsHeader));

@@ -7,24 +7,30 @@
 // over the unit's tokens, written as (m, l, o~) partials for the combine.
 //
 // How (MI355X-first):
-//  - One workgroup per compute unit streams a contiguous range of 32- or
-//    128-token tiles. Each tile [c | k^R] is copied HBM -> LDS once with
-//    LDS-DMA (global_load_lds_dwordx4) into a ring of STAGES buffers, so
-//    STAGES-1 tiles are in flight while one is consumed. The waits are
-//    explicit (s_waitcnt vmcnt), the loads are issued from inline asm so the
-//    compiler does not serialise them behind its own LDS alias checks.
+//  - One workgroup per compute unit streams a contiguous range of tiles of TT
+//    tokens. While tile x is computed from LDS, tile x+1 goes from registers
+//    into the other LDS buffer and tile x+2 is in flight from HBM into those
+//    registers (coalesced 16-byte global loads). One barrier per tile publishes
+//    the new tile and retires the old buffer. Rows past the sequence end are
+//    written as zeros on the way in. (Register staging rather than LDS-DMA:
+//    on gfx950 the DMA writes into LDS stall the MFMA operand reads.)
 //  - Every wave owns one (latent block, 16-head tile) task; all waves read the
 //    same LDS tile, so k^R and (for MLA) the latent are fetched from HBM once
 //    and shared by every head.
 //  - Scores: S^T[token][head] = K_ext[token] . Q_ext[head] with
 //    v_mfma_f32_16x16x32_bf16 (tokens as MFMA rows). Its output layout puts
 //    four tokens of one head in each lane, which is exactly the B-operand
-//    layout of the value product, so P never leaves registers.
+//    layout of the value product, so P never leaves registers. Per-head max
+//    and sum reduce across the four lanes of a head with v_permlane16/32_swap.
 //  - Values: O^T[col][head] += C^T[col][token] P^T[token][head], again
 //    16x16x32 bf16 MFMA; C^T operands come from 128-bit LDS reads of 8 token
 //    rows, transposed in registers with v_perm_b32.
 //  - Rows are XOR-swizzled in 16-byte chunks inside each 128-byte group
-//    (chunk ^ (row & 7)) so both read patterns are free of LDS bank conflicts.
+//    (chunk ^ (row & 7)) so both read patterns avoid LDS bank conflicts.
+//  - Page ids of the whole unit are gathered into LDS once, so the tile loop
+//    issues no scalar loads.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -32,10 +38,11 @@ namespace mlra {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int ST_>
+template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -43,7 +50,7 @@ struct Cfg {
   static constexpr int HT = HT_;    // 16-head tiles per block
   static constexpr int G = G_;      // waves sharing one task (token groups)
   static constexpr int TT = TT_;    // tokens per tile
-  static constexpr int ST = ST_;    // LDS ring stages
+  static constexpr int OCC = OCC_;  // workgroups resident per compute unit
   static constexpr int ROW = NBR * W + DR;
   static constexpr int ROWB = ROW * 2;
   static constexpr int CPR = ROW / 8;  // 16-byte chunks per row
@@ -51,80 +58,85 @@ struct Cfg {
   static constexpr int NWAVES = TASKS * G;
   static constexpr int NTHREADS = NWAVES * 64;
   static constexpr int TILE_BYTES = TT * ROWB;
-  static constexpr int NI = TT * CPR / 64;  // DMA instructions per tile
-  // Waves that issue DMA: the largest divisor of NI not above NWAVES, so every
-  // issuing wave has the same count (its vmcnt arithmetic stays static).
-  static constexpr int largest_divisor(int n, int cap) {
-    for (int d = cap; d > 1; --d)
-      if (n % d == 0) return d;
-    return 1;
+  static constexpr int TILE_CHUNKS = TT * CPR;
+  // Loader threads: the largest multiple of 64 not above NTHREADS that divides
+  // the tile's chunk count, so every loader moves the same number of chunks.
+  static constexpr int loaders() {
+    for (int n = NTHREADS; n >= 64; n -= 64)
+      if (TILE_CHUNKS % n == 0) return n;
+    return 64;
   }
-  static constexpr int NWD = largest_divisor(NI, NWAVES);
-  static constexpr int NI_W = NI / NWD;
-  static constexpr int KK = (W + DR) / 32;  // score k-steps
-  static constexpr int KKC = W / 32;        // k-steps over the latent part
+  static constexpr int NLT = loaders();
+  static constexpr int NL = TILE_CHUNKS / NLT;  // 16-byte chunks per loader per tile
+  static constexpr int KK = (W + DR) / 32;       // score k-steps
+  static constexpr int KKC = W / 32;             // k-steps over the latent part
   static constexpr int NSUB = TT / 32;
-  static constexpr int SUBW = NSUB / G;     // 32-token sub-tiles per wave per tile
-  static constexpr int NQ = W / 128;        // 128-column groups on the value side
+  static constexpr int SUBW = NSUB / G;          // 32-token sub-tiles per wave per tile
+  static constexpr int NQ = W / 128;             // 128-column groups on the value side
+  static constexpr int MAXPG = TT / 16;          // pages a tile can span (page_size >= 16)
+  static constexpr int SEQ_WIN = 64;
+  static constexpr int PT_CAP_RAW = (160 * 1024 / OCC - 2 * TILE_BYTES - SEQ_WIN * 4 - 256) / 4;
+  static constexpr int PT_CAP = PT_CAP_RAW > 4096 ? 4096 : PT_CAP_RAW;
   static_assert(ROW % 64 == 0, "rows must be whole 128-byte groups");
   static_assert(W % 128 == 0 && DR % 32 == 0, "");
   static_assert(TT % 32 == 0 && NSUB % G == 0, "");
-  static_assert(NI * 64 == TT * CPR && NI % NWD == 0, "");
-  static_assert((ST - 1) * NI_W <= 63, "vmcnt range");
-  static_assert(ST * TILE_BYTES <= 160 * 1024, "LDS");
+  static_assert(TILE_CHUNKS % NLT == 0, "");
+  static_assert(PT_CAP >= 64, "LDS: room for the page-id table");
   static_assert(NTHREADS <= 1024, "");
 };
 
-// One LDS-DMA instruction: lane l copies 16 bytes from base + off to LDS
-// address lds_addr + 16 l. m0 is saved and restored around it.
-__device__ __forceinline__ void dma16(uint64_t base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int STAGES, int NIW>
-__device__ __forceinline__ void wait_tile(int tiles_after) {
-  // Each wave issued NIW loads per tile; waiting until at most
-  // tiles_after * NIW remain guarantees this tile has landed.
-  switch (tiles_after) {
-    case 0: wait_vmcnt_barrier<0>(); break;
-    case 1: wait_vmcnt_barrier<NIW>(); break;
-    case 2: if constexpr (STAGES > 2) wait_vmcnt_barrier<2 * NIW>(); break;
-    case 3: if constexpr (STAGES > 3) wait_vmcnt_barrier<3 * NIW>(); break;
-    case 4: if constexpr (STAGES > 4) wait_vmcnt_barrier<4 * NIW>(); break;
-    case 5: if constexpr (STAGES > 5) wait_vmcnt_barrier<5 * NIW>(); break;
-    default: wait_vmcnt_barrier<0>(); break;
-  }
-}
+// Uniform 32-bit load through the scalar cache (constant address space).
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
+__device__ __forceinline__ int32_t cload(const int32_t* p) { return *(cint32_t*)(p); }
 
 __device__ __forceinline__ floatx4_t mfma32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the lanes holding one head).
+__device__ __forceinline__ float max_4lanes(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_4lanes(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 16-byte load from global memory (explicit address space: a generic pointer
+// would compile to a flat load, which the compiler must also wait for with
+// lgkmcnt before any LDS result can be used).
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+__device__ __forceinline__ u32x4_t gload16(const uint8_t* p) { return *(const gu32x4_t*)(p); }
+
+__device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::ST * C::TILE_BYTES];
+__global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::TILE_BYTES];
+  __shared__ int32_t ptab[C::PT_CAP];      // physical page of (tile - x0, page in tile)
+  __shared__ int32_t seq_end[C::SEQ_WIN];  // cum[lo + 1 + i]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -143,9 +155,10 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
   const int HK = a.n_heads * a.k;
   const int hk = head * a.k + jj;
   const int P = a.page_size;
+  const bool loader = tid < C::NLT;
 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
-  const int32_t NT = hdr->n_tiles;
+  const int32_t NT = cload(&hdr->n_tiles);
   const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
   const int32_t* nlen = reinterpret_cast<const int32_t*>(a.ws + a.off_nlen);
   const int unit = blockIdx.x;
@@ -157,64 +170,84 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
   int lo = 0, hi = a.batch - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (cum[mid] <= x0) lo = mid; else hi = mid - 1;
+    if (cload(cum + mid) <= x0) lo = mid; else hi = mid - 1;
   }
 
-  // Per-lane byte offsets of this wave's DMA slots inside a contiguous tile image.
-  uint32_t loff[C::NI_W];
-#pragma unroll
-  for (int k = 0; k < C::NI_W; ++k) {
-    const int p = (k * C::NWD + wave) * 64 + lane;
-    const int r = p / C::CPR;
-    const int lc = (p % C::CPR) ^ (r & 7);
-    loff[k] = static_cast<uint32_t>(r * C::ROWB + 16 * lc);
-  }
-  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  const uint64_t pool = reinterpret_cast<uint64_t>(a.pool);
-
-  // Issue cursor (runs STAGES-1 tiles ahead of the compute cursor).
-  int ib = lo;
-  int32_t ib_start = cum[ib], ib_end = cum[ib + 1], ib_n = nlen[ib];
+  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
   uint32_t bad_page = 0;
+  const int npt = P >= C::TT ? 1 : C::TT >> a.log2_page;  // pages per tile
 
-  auto issue = [&](int32_t x, int stage) {
-    while (x >= ib_end) {
-      ++ib;
-      ib_start = ib_end;
-      ib_end = cum[ib + 1];
-      ib_n = nlen[ib];
+  // ---- load cursor: runs two tiles ahead of the compute cursor
+  int pb = lo;
+  int32_t pb_start = cload(cum + pb), pb_end = cload(cum + pb + 1), pb_n = cload(nlen + pb);
+  bool use_tab = false;
+  auto lookup = [&](int b, int32_t pidx) __attribute__((always_inline)) -> int32_t {
+    int32_t phys = a.page_table ? cload(a.page_table + static_cast<int64_t>(b) * a.max_pages + pidx)
+                                : b * a.max_pages + pidx;
+    if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) {
+      phys = 0;
+      bad_page = 1;
     }
-    if (wave >= C::NWD) return;
-    const int32_t tok0 = (x - ib_start) * C::TT;
-    const int32_t npg = (ib_n + P - 1) >> a.log2_page;
+    return phys;
+  };
+  // Physical page of the j-th page of tile x (x at the load cursor).
+  auto page_of = [&](int32_t x, int j) __attribute__((always_inline)) -> int32_t {
+    if (use_tab) return __builtin_amdgcn_readfirstlane(ptab[(x - x0) * npt + j]);
+    const int32_t npg = (pb_n + P - 1) >> a.log2_page;
+    const int32_t pg = ((((x - pb_start) * C::TT)) >> a.log2_page) + j;
+    return lookup(pb, pg < npg ? pg : npg - 1);
+  };
+  // Issues the global loads of tile x into ring slot `ring`.
+  auto load_tile = [&](int32_t x, u32x4_t* ring) __attribute__((always_inline)) {
+    while (x >= pb_end) {
+      ++pb;
+      pb_start = pb_end;
+      pb_end = cload(cum + pb + 1);
+      pb_n = cload(nlen + pb);
+    }
+    if (!loader) return;
+    const int32_t tok0 = (x - pb_start) * C::TT;
+    if (P >= C::TT) {
+      // the whole tile sits in one page: one base, per-lane offsets
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(
+          pool + (static_cast<int64_t>(page_of(x, 0)) * P + (tok0 & (P - 1))) * C::ROWB)));
 #pragma unroll
-    for (int k = 0; k < C::NI_W; ++k) {
-      const int inst = k * C::NWD + wave;
-      const int row0 = (inst * 64) / C::CPR;
-      const int32_t pg_unclamped = (tok0 + row0) >> a.log2_page;
-      const int32_t pidx = pg_unclamped < npg ? pg_unclamped : npg - 1;
-      int32_t phys = a.page_table ? a.page_table[static_cast<int64_t>(ib) * a.max_pages + pidx]
-                                  : ib * a.max_pages + pidx;
-      if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) {
-        phys = 0;
-        bad_page = 1;
+      for (int k = 0; k < C::NL; ++k) {
+        const int p = k * C::NLT + tid;
+        const int r = p / C::CPR, lc = p % C::CPR;
+        ring[k] = gload16(base + r * C::ROWB + 16 * lc);
       }
-      uint32_t off;
-      if (P >= C::TT) {
-        off = loff[k] + static_cast<uint32_t>((tok0 & (P - 1)) * C::ROWB);
-      } else {
-        const int32_t first_pg = tok0 >> a.log2_page;
-        off = loff[k] - static_cast<uint32_t>((pg_unclamped - first_pg) * P * C::ROWB);
+    } else {
+      // tile spans npt pages (tok0 is page aligned): per-lane page select
+      int32_t ph[C::MAXPG];
+#pragma unroll
+      for (int j = 0; j < C::MAXPG; ++j) ph[j] = j < npt ? page_of(x, j) : 0;
+#pragma unroll
+      for (int k = 0; k < C::NL; ++k) {
+        const int p = k * C::NLT + tid;
+        const int r = p / C::CPR, lc = p % C::CPR;
+        const int j = r >> a.log2_page;
+        int32_t phys = ph[0];
+#pragma unroll
+        for (int q = 1; q < C::MAXPG; ++q) phys = j == q ? ph[q] : phys;
+        ring[k] = gload16(pool + (static_cast<int64_t>(phys) * P + (r & (P - 1))) * C::ROWB + 16 * lc);
       }
-      const uint64_t base = pool + static_cast<uint64_t>(phys) * static_cast<uint64_t>(P) * C::ROWB;
-      const uint32_t b_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base));
-      const uint32_t b_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32));
-      dma16((static_cast<uint64_t>(b_hi) << 32) | b_lo, off,
-            __builtin_amdgcn_readfirstlane(lds_base + stage * C::TILE_BYTES + inst * 1024));
+    }
+  };
+  // Writes ring slot `ring` (tile with `valid` token rows) into LDS buffer `dst`.
+  auto store_tile = [&](const u32x4_t* ring, uint8_t* dst, int valid) __attribute__((always_inline)) {
+    if (!loader) return;
+#pragma unroll
+    for (int k = 0; k < C::NL; ++k) {
+      const int p = k * C::NLT + tid;
+      const int r = p / C::CPR, lc = p % C::CPR;
+      u32x4_t v = ring[k];
+      if (r >= valid) v = u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (lc ^ (r & 7))) = v;
     }
   };
 
-  // Compute state.
+  // ---- compute state
   floatx4_t O[C::NQ][8];
 #pragma unroll
   for (int q = 0; q < C::NQ; ++q)
@@ -224,74 +257,140 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
   bf16x8_t Qb[C::KK];
 
   int cb = lo;
-  int32_t cb_start = cum[cb], cb_end = cum[cb + 1], cb_n = nlen[cb];
-  bool need_q = true;
+  int32_t cb_start = pb_start, cb_end = pb_end, cb_n = pb_n;
 
   float* pm = reinterpret_cast<float*>(a.ws + a.off_pm);
   float* pl = reinterpret_cast<float*>(a.ws + a.off_pl);
   float* po = reinterpret_cast<float*>(a.ws + a.off_po);
   const uint16_t* qext = reinterpret_cast<const uint16_t*>(a.ws + a.off_qext);
 
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const uint16_t* qe = qext + (static_cast<int64_t>(b) * HK + hk) * (C::W + C::DR);
 #pragma unroll
-  for (int s = 0; s < C::ST - 1; ++s)
-    if (x0 + s < x1) issue(x0 + s, s);
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const int off = kk < C::KKC ? 32 * kk + 8 * g4 : C::W + 32 * (kk - C::KKC) + 8 * g4;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (head_ok) v = gload16(reinterpret_cast<const uint8_t*>(qe + off));
+      Qb[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  };
+  load_q(cb);
 
-  for (int32_t x = x0; x < x1; ++x) {
+  // ---- store cursor: the tile written into LDS next
+  int sc_b = lo;
+  int32_t sc_start = pb_start, sc_end = pb_end, sc_n = pb_n;
+  auto store_valid = [&](int32_t x) __attribute__((always_inline)) -> int {
+    while (x >= sc_end) {
+      ++sc_b;
+      sc_start = sc_end;
+      sc_end = cload(cum + sc_b + 1);
+      sc_n = cload(nlen + sc_b);
+    }
+    return min(C::TT, sc_n - (x - sc_start) * C::TT);
+  };
+
+  // ---- prologue: tile x0 into LDS buffer 0, tile x0+1 in flight
+  u32x4_t ring[C::NL];
+  load_tile(x0, ring);
+  store_tile(ring, lds, store_valid(x0));
+  if (x0 + 1 < x1) load_tile(x0 + 1, ring);
+
+  // ---- page ids of the rest of the unit, gathered into LDS while tile x0+1
+  // is in flight
+  {
+    const int win = min(C::SEQ_WIN, a.batch - lo);
+    if (tid < win) seq_end[tid] = cum[lo + 1 + tid];
+    __syncthreads();
+    const int32_t ntab = (x1 - x0) * npt;
+    if (ntab <= C::PT_CAP && x1 <= seq_end[win - 1]) {
+      const int32_t lo_start = cb_start;
+      for (int i = tid; i < ntab; i += C::NTHREADS) {
+        const int32_t x = x0 + i / npt;
+        const int j = i % npt;
+        int k = 0;
+        while (seq_end[k] <= x) ++k;
+        const int b = lo + k;
+        const int32_t start = k == 0 ? lo_start : seq_end[k - 1];
+        const int32_t n = nlen[b];
+        const int32_t npg = (n + P - 1) >> a.log2_page;
+        const int32_t pg0 = (((x - start) * C::TT) >> a.log2_page) + j;
+        const int32_t pg = pg0 < npg ? pg0 : npg - 1;
+        int32_t phys = a.page_table ? a.page_table[static_cast<int64_t>(b) * a.max_pages + pg]
+                                    : b * a.max_pages + pg;
+        if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) {
+          phys = 0;
+          bad_page = 1;
+        }
+        ptab[i] = phys;
+      }
+      use_tab = true;
+    }
+    __syncthreads();
+  }
+
+  auto step = [&](int32_t x) __attribute__((always_inline)) {
     const int t = x - x0;
-    const int st = t % C::ST;
-    if (x + C::ST - 1 < x1) issue(x + C::ST - 1, (t + C::ST - 1) % C::ST);
-    const int after = wave < C::NWD ? min(C::ST - 1, x1 - 1 - x) : 0;
-    wait_tile<C::ST, C::NI_W>(after);
+    uint8_t* sb = lds + (t & 1) * C::TILE_BYTES;
 
+    bool need_q = false;
     while (x >= cb_end) {
       ++cb;
       cb_start = cb_end;
-      cb_end = cum[cb + 1];
-      cb_n = nlen[cb];
+      cb_end = cload(cum + cb + 1);
+      cb_n = cload(nlen + cb);
       need_q = true;
     }
     const int valid = min(C::TT, cb_n - (x - cb_start) * C::TT);
-    uint8_t* sb = lds + st * C::TILE_BYTES;
-    if (valid < C::TT) {
-      // Rows past the sequence end may hold anything: zero them so that the
-      // value product sees 0 * 0 there.
-      const int nz = (C::TT - valid) * C::CPR;
-      for (int idx = tid; idx < nz; idx += C::NTHREADS) {
-        const int r = valid + idx / C::CPR;
-        *reinterpret_cast<u32x4_t*>(sb + r * C::ROWB + 16 * (idx % C::CPR)) = u32x4_t{0u, 0u, 0u, 0u};
-      }
-      lds_barrier();
+    // Tile x is in its buffer for every wave and every wave is done with
+    // tile x-1: tile x+1 goes registers -> the other buffer, tile x+2 is
+    // requested into the registers.
+    lds_barrier();
+    if (x + 1 < x1) {
+      store_tile(ring, lds + ((t + 1) & 1) * C::TILE_BYTES, store_valid(x + 1));
+      if (x + 2 < x1) load_tile(x + 2, ring);
     }
-    if (need_q) {
-      const uint16_t* qe = qext + (static_cast<int64_t>(cb) * HK + hk) * (C::W + C::DR);
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const int off = kk < C::KKC ? 32 * kk + 8 * g4 : C::W + 32 * (kk - C::KKC) + 8 * g4;
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (head_ok) v = *reinterpret_cast<const u32x4_t*>(qe + off);
-        Qb[kk] = __builtin_bit_cast(bf16x8_t, v);
-      }
-      need_q = false;
-    }
+    if (need_q) load_q(cb);  // a new sequence starts inside this unit
 
 #pragma unroll
     for (int si = 0; si < C::SUBW; ++si) {
       const int rowbase = 32 * (si * C::G + tgrp);
       // ---- scores: S_h[i] = token rowbase + 16 h + 4 g4 + i, head m16
-      floatx4_t S0 = floatx4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0;
       const int r0 = rowbase + m16;
       const uint8_t* rp0 = sb + r0 * C::ROWB;
       const uint8_t* rp1 = rp0 + 16 * C::ROWB;
       const int key = m16 & 7;
+      floatx4_t S0 = floatx4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+      constexpr int KB = 3;  // score k-steps whose operands are read ahead together
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const int chunk = kk < C::KKC ? blk * (C::W / 8) + 4 * kk + g4
-                                      : C::NBR * (C::W / 8) + 4 * (kk - C::KKC) + g4;
-        const int co = 16 * (chunk ^ key);
-        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(rp0 + co));
-        const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(rp1 + co));
-        S0 = mfma32(a0, Qb[kk], S0);
-        S1 = mfma32(a1, Qb[kk], S1);
+      for (int kb = 0; kb < C::KK; kb += KB) {
+        u32x4_t A0[KB], A1[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int kk = kb + u;
+          if (kk < C::KK) {
+            const int chunk = kk < C::KKC ? blk * (C::W / 8) + 4 * kk + g4
+                                          : C::NBR * (C::W / 8) + 4 * (kk - C::KKC) + g4;
+            const int co = 16 * (chunk ^ key);
+            A0[u] = lds_read16(rp0 + co);
+            A1[u] = lds_read16(rp1 + co);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int kk = kb + u;
+          if (kk < C::KK) {
+            S0 = mfma32(__builtin_bit_cast(bf16x8_t, A0[u]), Qb[kk], S0);
+            S1 = mfma32(__builtin_bit_cast(bf16x8_t, A1[u]), Qb[kk], S1);
+          }
+        }
+      }
+      // value-side rows of the first 128-column group, read while the scores finish
+      const int vchunk0 = blk * (C::W / 8) + m16;
+      u32x4_t R[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
+        R[v] = lds_read16(sb + tr * C::ROWB + 16 * (vchunk0 ^ (tr & 7)));
       }
       if (valid < C::TT) {
 #pragma unroll
@@ -303,8 +402,7 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
       // ---- online softmax (per head m16; lanes m16, m16+16, +32, +48 share a head)
       float mx = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
                        fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_4lanes(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float scale = fast_exp2(m_run - m_use);
@@ -330,29 +428,29 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
       // ---- values: O^T[col][head] += C^T[col][tokens] P^T[tokens][head]
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) {
-        const int chunk = blk * (C::W / 8) + 16 * q + m16;
-        u32x4_t R[8];
+        if (q > 0) {
+          const int chunk = blk * (C::W / 8) + 16 * q + m16;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
-          R[v] = *reinterpret_cast<const u32x4_t*>(sb + tr * C::ROWB + 16 * (chunk ^ (tr & 7)));
+          for (int v = 0; v < 8; ++v) {
+            const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
+            R[v] = lds_read16(sb + tr * C::ROWB + 16 * (chunk ^ (tr & 7)));
+          }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x4_t A;
+          u32x4_t Av;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            A[u] = __builtin_amdgcn_perm(R[2 * u + 1][e >> 1], R[2 * u][e >> 1], sel);
-          O[q][e] = mfma32(__builtin_bit_cast(bf16x8_t, A), pb, O[q][e]);
+            Av[u] = __builtin_amdgcn_perm(R[2 * u + 1][e >> 1], R[2 * u][e >> 1], sel);
+          O[q][e] = mfma32(__builtin_bit_cast(bf16x8_t, Av), pb, O[q][e]);
         }
       }
     }
 
     if (x + 1 == cb_end || x + 1 == x1) {
       // ---- segment end: write this wave's partial and reset.
-      float l_tot = l_run + __shfl_xor(l_run, 16);
-      l_tot += __shfl_xor(l_tot, 32);
+      const float l_tot = sum_4lanes(l_run);
       const int64_t slot = static_cast<int64_t>(unit + cb) * C::G + tgrp;
       if (head_ok) {
         float* dst = po + (slot * HK + hk) * C::W;
@@ -374,9 +472,10 @@ __global__ __launch_bounds__(C::NTHREADS, 1) void attend_mfma_kernel(DecodeArgs 
       m_run = -INFINITY;
       l_run = 0.f;
     }
-    lds_barrier();
-  }
-  if (bad_page && lane == 0) atomicOr(&hdr->flags, kFlagBadPage);
+  };
+
+  for (int32_t x = x0; x < x1; ++x) step(x);
+  if (__any(bad_page) && lane == 0) atomicOr(&hdr->flags, kFlagBadPage);
 }
 
 template <class C>
@@ -390,22 +489,21 @@ struct Entry {
   hipError_t (*fn)(const DecodeArgs&, hipStream_t);
 };
 
-template <int W, int DR, int NBR, int HT, int G, int TT, int ST>
+template <int W, int DR, int NBR, int HT, int G, int TT, int OCC>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, ST>;
-  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, ST, C::NTHREADS, C::ST * C::TILE_BYTES},
-               &run_variant<C>};
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC>;
+  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, C::NTHREADS, 2 * C::TILE_BYTES}, &run_variant<C>};
 }
 
 // Shapes with a tuned MFMA kernel. Key: (w, d_r, blocks per row, 16-head tiles per block).
 const Entry kVariants[] = {
-    entry<128, 64, 4, 1, 1, 32, 4>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
-    entry<512, 64, 1, 4, 1, 32, 4>(),   // MLA: one 512 latent, 64 heads
-    entry<128, 64, 1, 1, 4, 128, 3>(),  // one MLRA-4 block (a TP rank's share), <= 16 heads
-    entry<256, 64, 2, 2, 1, 32, 4>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
-    entry<128, 64, 4, 2, 1, 32, 4>(),   // 4 x 128 latent, <= 32 heads per block
-    entry<128, 64, 4, 4, 1, 32, 4>(),   // 4 x 128 latent, <= 64 heads per block
-    entry<256, 64, 1, 2, 2, 64, 4>(),   // one 256 block + RoPE, <= 32 heads
+    entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
+    entry<512, 64, 1, 4, 1, 32, 1>(),   // MLA: one 512 latent, 64 heads
+    entry<128, 64, 1, 1, 4, 128, 1>(),  // one MLRA-4 block (a TP rank's share), <= 16 heads
+    entry<256, 64, 2, 2, 1, 32, 1>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
+    entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
+    entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
+    entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
 };
 
 }  // namespace

@@ -10,7 +10,7 @@ namespace mlra {
 // Tuning of one MFMA attention variant (see attend_mfma.hip).
 struct MfmaVariant {
   int w, d_r, n_blocks, head_tiles;  // shape key
-  int groups, tile_tokens, stages;    // tuning
+  int groups, tile_tokens, occupancy;  // tuning (occupancy: workgroups per compute unit)
   int threads;
   int lds_bytes;
 };
