@@ -45,6 +45,18 @@ __device__ void write_plan(const DecodeArgs& a, const int32_t* seq_lens) {
     carry += scan_sh[kAbsorbThreads - 1];
     __syncthreads();
   }
+  // the empty partial slot read by the combine for slots no unit wrote
+  {
+    const int hk_all = a.n_heads * a.k;
+    float* pm = reinterpret_cast<float*>(a.ws + a.off_pm) + static_cast<int64_t>(a.empty_slot) * hk_all;
+    float* pl = reinterpret_cast<float*>(a.ws + a.off_pl) + static_cast<int64_t>(a.empty_slot) * hk_all;
+    float* po = reinterpret_cast<float*>(a.ws + a.off_po) + static_cast<int64_t>(a.empty_slot) * hk_all * a.w;
+    for (int i = tid; i < hk_all; i += kAbsorbThreads) {
+      pm[i] = -INFINITY;
+      pl[i] = 0.f;
+    }
+    for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
+  }
   if (tid == 0) {
     cum[a.batch] = carry;
     WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);

@@ -50,7 +50,7 @@ int make_plan(const mlra_desc* d, Plan* p) {
     p->q_bf16 = false;
   }
   p->units = compute_units() * (p->variant ? p->variant->occupancy : 1);
-  p->slots = static_cast<int64_t>(p->units + d->batch) * p->groups;
+  p->slots = static_cast<int64_t>(p->units + d->batch) * p->groups + 1;  // + the empty slot
   const size_t qelem = p->q_bf16 ? 2 : 4;
   size_t off = align_up(sizeof(WsHeader));
   p->off_cum = off;
@@ -98,6 +98,7 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.units = p.units;
   a.tile_tokens = p.tile_tokens;
   a.groups = p.groups;
+  a.empty_slot = static_cast<int32_t>(p.slots - 1);
   const float sigma = d->softmax_scale > 0.f ? d->softmax_scale
                                              : 1.0f / sqrtf(static_cast<float>(d->d_h + d->d_r));
   a.qscale = sigma * 1.4426950408889634f;
@@ -203,6 +204,7 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   c.w = p.s.w;
   c.k = desc->blocks_per_head;
   c.hk = p.s.hk;
+  c.empty_slot = static_cast<int32_t>(p.slots - 1);
   c.out_scale = desc->out_scale > 0.f ? desc->out_scale
                                       : 1.0f / sqrtf(static_cast<float>(desc->blocks_per_head));
   return hip_status(launch_combine(c, desc->dtype, static_cast<hipStream_t>(stream)));

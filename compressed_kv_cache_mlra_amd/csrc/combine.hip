@@ -10,12 +10,15 @@
 // combined", alanhou.org "Core Mechanism").
 //
 // One workgroup per (head, group of 8 sequences). The partials were just
-// written by other compute units, so every read is an L2/MALL round trip:
-// all (sequence, block) pairs are merged at once, each by 32 threads, with
-// branch-free slot loops so the loads of one thread are all in flight
-// together. W^UV[head] is then read once per workgroup and applied to the 8
-// merged latents, which sit in LDS transposed ([k w][8]) so one W^UV element
-// meets all 8 with two 16-byte LDS reads.
+// written by other compute units, so every read is an L2/MALL round trip; the
+// kernel is organised so that each thread has all its reads in flight at once:
+// the W^UV slice a thread needs is requested first, then each thread merges
+// four columns of one (sequence, block) pair from 16 partial slots per batch
+// (it recomputes the pair's max and sum itself rather than waiting on other
+// threads). The merged latents sit in LDS transposed ([k w][8]) so each W^UV
+// element meets all 8 sequences with two 16-byte LDS reads.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -24,121 +27,159 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatchGroup = 8;
-constexpr int kPairLanes = 32;                     // threads per (sequence, block) pair
-constexpr int kPairsPerPass = kThreads / kPairLanes;
+constexpr int kSlotBatch = 16;  // partial slots whose loads are in flight together
+constexpr int kWPrefetch = 32;  // W^UV rows per thread loaded ahead of the merge
 
-// Reduction over the 32 lanes of a half-wave (xor 16, 8, 4, 2, 1).
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int off = 16; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 32));
-  return v;
+// Two adjacent W^UV elements (d, d+1) as floats. EVEN: d_h is even, so the
+// pair is one aligned 4-byte (bf16) or 8-byte (fp32) load; otherwise two
+// scalar loads, the second from a clamped index. No branches, so every load
+// of a loop can be in flight at once.
+template <typename TW, bool EVEN>
+__device__ __forceinline__ float2 load_pair(const TW* p, int64_t i, int64_t i2);
+template <>
+__device__ __forceinline__ float2 load_pair<uint16_t, true>(const uint16_t* p, int64_t i, int64_t) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p + i);
+  return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
 }
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int off = 16; off > 0; off >>= 1) v += __shfl_xor(v, off, 32);
-  return v;
+template <>
+__device__ __forceinline__ float2 load_pair<uint16_t, false>(const uint16_t* p, int64_t i, int64_t i2) {
+  return make_float2(bf16_to_f32(p[i]), bf16_to_f32(p[i2]));
+}
+template <>
+__device__ __forceinline__ float2 load_pair<float, true>(const float* p, int64_t i, int64_t) {
+  return *reinterpret_cast<const float2*>(p + i);
+}
+template <>
+__device__ __forceinline__ float2 load_pair<float, false>(const float* p, int64_t i, int64_t i2) {
+  return make_float2(p[i], p[i2]);
 }
 
-template <typename TW>
+template <typename TW, bool EVEN>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   extern __shared__ float sh[];
   float* ot = sh;                             // [k * w][kBatchGroup]
   float* red = sh + kBatchGroup * a.k * a.w;  // [kThreads][2 * kBatchGroup]
-  float* mstat = red + kThreads * 2 * kBatchGroup;  // [kBatchGroup * k][2]: M, 1 / L
   __shared__ int32_t sinfo[kBatchGroup][2];   // per sequence: first, last unit (last < first: empty)
 
   const int tid = threadIdx.x;
   const int head = blockIdx.x;
   const int b0 = blockIdx.y * kBatchGroup;
   const int nb = min(kBatchGroup, a.batch - b0);
+  const int KW = a.k * a.w;
+
+  // ---- W^UV slice of this thread, requested before anything else
+  // thread -> (output column pair dp, e-slice part); passes over column pairs
+  // beyond the first 256 reload inside the product loop.
+  const TW* wuv = static_cast<const TW*>(a.w_uv) + static_cast<int64_t>(head) * KW * a.d_h;
+  const int pairs_d = (a.d_h + 1) / 2;
+  const int span0 = min(kThreads, pairs_d);
+  const int split0 = max(1, kThreads / span0);
+  const int part0 = tid / span0;
+  const int d_0 = 2 * (tid % span0);
+  const int e0_0 = static_cast<int>((static_cast<int64_t>(part0) * KW) / split0);
+  const int e1_0 = static_cast<int>((static_cast<int64_t>(part0 + 1) * KW) / split0);
+  const int d_0b = min(d_0 + 1, a.d_h - 1);
+  float2 wpre[kWPrefetch];
+#pragma unroll
+  for (int u = 0; u < kWPrefetch; ++u) {
+    const int e = min(e0_0 + u, KW - 1);  // rows past the slice are loaded but not used
+    wpre[u] = load_pair<TW, EVEN>(wuv, static_cast<int64_t>(e) * a.d_h + d_0,
+                                  static_cast<int64_t>(e) * a.d_h + d_0b);
+  }
+
+  // header through the scalar cache, so using it does not wait for the W^UV loads
+  typedef __attribute__((address_space(4))) const int32_t cint32_t;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
-  const int32_t NT = hdr->n_tiles, units = hdr->units, G = hdr->groups;
+  const int32_t NT = *(cint32_t*)(&hdr->n_tiles), units = *(cint32_t*)(&hdr->units);
+  const int32_t G = *(cint32_t*)(&hdr->groups);
   const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
   const float* pm = reinterpret_cast<const float*>(a.ws + a.off_pm);
   const float* pl = reinterpret_cast<const float*>(a.ws + a.off_pl);
   const float* po = reinterpret_cast<const float*>(a.ws + a.off_po);
-  const int KW = a.k * a.w;
-  const int npairs = nb * a.k;
+  const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;  // first entry of the empty slot
 
-  if (tid < kBatchGroup) {
-    int32_t u0 = 0, u1 = -1;
-    if (tid < nb) {
-      const int32_t xa = cum[b0 + tid], xb = cum[b0 + tid + 1];
-      if (xa < xb) {
-        u0 = unit_of_tile(xa, NT, units);
-        u1 = unit_of_tile(xb - 1, NT, units);
+  if (tid == 0) {
+    for (int bl = 0; bl < kBatchGroup; ++bl) {
+      int32_t u0 = 0, u1 = -1;
+      if (bl < nb) {
+        const int32_t xa = *(cint32_t*)(cum + b0 + bl), xb = *(cint32_t*)(cum + b0 + bl + 1);
+        if (xa < xb) {
+          u0 = unit_of_tile(xa, NT, units);
+          u1 = unit_of_tile(xb - 1, NT, units);
+        }
       }
+      sinfo[bl][0] = u0;
+      sinfo[bl][1] = u1;
     }
-    sinfo[tid][0] = u0;
-    sinfo[tid][1] = u1;
   }
   __syncthreads();
 
-  // ---- M and 1/L per (sequence, block) pair: 32 threads per pair, slots strided
-  for (int p0 = 0; p0 < npairs; p0 += kPairsPerPass) {
-    const int p = p0 + tid / kPairLanes;
-    const int ln = tid % kPairLanes;
-    const bool live = p < npairs;
-    const int bl = live ? p / a.k : 0, jj = live ? p % a.k : 0;
-    const int b = b0 + bl, hk = head * a.k + jj;
-    const int32_t u0 = sinfo[bl][0];
-    const int nslots = live ? (sinfo[bl][1] - u0 + 1) * G : 0;
-    float M = -INFINITY;
-    for (int s = ln; s < nslots; s += kPairLanes) {
-      const int32_t u = u0 + s / G;
-      const float v = pm[(static_cast<int64_t>(u + b) * G + s % G) * a.hk + hk];
-      if (unit_owns_tiles(u, NT, units)) M = fmaxf(M, v);
-    }
-    M = half_max(M);
-    const float Muse = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    for (int s = ln; s < nslots; s += kPairLanes) {
-      const int32_t u = u0 + s / G;
-      const int64_t idx = (static_cast<int64_t>(u + b) * G + s % G) * a.hk + hk;
-      const float v = pl[idx] * fast_exp2(pm[idx] - Muse);
-      if (unit_owns_tiles(u, NT, units)) L += v;
-    }
-    L = half_sum(L);
-    if (live && ln == 0) {
-      mstat[2 * p] = Muse;
-      mstat[2 * p + 1] = nslots > 0 ? 1.f / L : 0.f;
-      if (a.lse)
+  // ---- merge: item = (pair, 4 columns); 16 slots of loads in flight per batch
+  const int w4 = a.w / 4;
+  const int npairs = nb * a.k;
+  // When there are at least as many tiles as units every unit owns tiles and
+  // the per-slot check (64-bit divisions) is skipped.
+  auto merge = [&](auto check_units) __attribute__((always_inline)) {
+    constexpr bool kCheck = decltype(check_units)::value;
+  for (int it = tid; it < npairs * w4; it += kThreads) {
+      const int p = it / w4, c = 4 * (it % w4);
+      const int bl = p / a.k, jj = p % a.k;
+      const int b = b0 + bl, hk = head * a.k + jj;
+      const int32_t u0 = sinfo[bl][0];
+      const int nslots = (sinfo[bl][1] - u0 + 1) * G;
+      float M = -INFINITY, L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s0 = 0; s0 < nslots; s0 += kSlotBatch) {
+        float ms[kSlotBatch], ls[kSlotBatch];
+        float4 vs[kSlotBatch];
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          const int s = s0 + u;
+          const int32_t uu = u0 + s / G;
+          // units with an empty range (fewer tiles than units) wrote nothing
+          const bool ok = s < nslots && (!kCheck || unit_owns_tiles(uu, NT, units));
+          // invalid slots read the empty partial (m = -inf, l = 0, o~ = 0)
+          const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + s % G) * a.hk + hk : empty_hk + hk;
+          ms[u] = pm[idx];
+          ls[u] = pl[idx];
+          vs[u] = *reinterpret_cast<const float4*>(po + idx * a.w + c);
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) mb = fmaxf(mb, ms[u]);
+        const float mu = mb == -INFINITY ? 0.f : mb;
+        const float r = fast_exp2(M - mu);
+        L *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+          const float wgt = fast_exp2(ms[u] - mu);  // 0 for empty slots (m = -inf)
+          L += wgt * ls[u];
+          acc.x += wgt * vs[u].x;
+          acc.y += wgt * vs[u].y;
+          acc.z += wgt * vs[u].z;
+          acc.w += wgt * vs[u].w;
+        }
+        M = mb;
+      }
+      const float invL = nslots > 0 ? 1.f / L : 0.f;
+      if (c == 0 && a.lse)
         a.lse[(static_cast<int64_t>(b) * a.n_heads + head) * a.k + jj] =
             nslots > 0 ? 0.69314718055994531f * (M + __log2f(L)) : -INFINITY;
+      const int e = jj * a.w + c;
+      ot[(e + 0) * kBatchGroup + bl] = acc.x * invL;
+      ot[(e + 1) * kBatchGroup + bl] = acc.y * invL;
+      ot[(e + 2) * kBatchGroup + bl] = acc.z * invL;
+      ot[(e + 3) * kBatchGroup + bl] = acc.w * invL;
     }
-  }
-  __syncthreads();
-
-  // ---- merged latents: item = (pair, 4 columns); loads of all slots in flight
-  const int w4 = a.w / 4;
-  for (int it = tid; it < npairs * w4; it += kThreads) {
-    const int p = it / w4, c = 4 * (it % w4);
-    const int bl = p / a.k, jj = p % a.k;
-    const int b = b0 + bl, hk = head * a.k + jj;
-    const int32_t u0 = sinfo[bl][0];
-    const int nslots = (sinfo[bl][1] - u0 + 1) * G;
-    const float M = mstat[2 * p];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-    for (int s = 0; s < nslots; ++s) {
-      const int32_t u = u0 + s / G;
-      const int64_t idx = (static_cast<int64_t>(u + b) * G + s % G) * a.hk + hk;
-      const float4 v = *reinterpret_cast<const float4*>(po + idx * a.w + c);
-      // units with an empty range (fewer tiles than units) wrote nothing
-      const float wgt = unit_owns_tiles(u, NT, units) ? fast_exp2(pm[idx] - M) : 0.f;
-      const bool ok = wgt != 0.f;
-      acc.x += ok ? wgt * v.x : 0.f;
-      acc.y += ok ? wgt * v.y : 0.f;
-      acc.z += ok ? wgt * v.z : 0.f;
-      acc.w += ok ? wgt * v.w : 0.f;
-    }
-    const float invL = mstat[2 * p + 1];
-    const int e = jj * a.w + c;
-    ot[(e + 0) * kBatchGroup + bl] = acc.x * invL;
-    ot[(e + 1) * kBatchGroup + bl] = acc.y * invL;
-    ot[(e + 2) * kBatchGroup + bl] = acc.z * invL;
-    ot[(e + 3) * kBatchGroup + bl] = acc.w * invL;
-  }
+  };
+  if (NT >= units)
+    merge(std::false_type{});
+  else
+    merge(std::true_type{});
   for (int it = tid; it < (kBatchGroup - nb) * KW; it += kThreads) {
     const int bl = nb + it / KW, e = it % KW;
     ot[e * kBatchGroup + bl] = 0.f;
@@ -147,8 +188,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
   // ---- out[b][head][d] = out_scale * sum_e W^UV[head][e][d] o~[b][e],  e = (jj, c)
   // Each thread owns two adjacent output columns and a slice of e.
-  const TW* wuv = static_cast<const TW*>(a.w_uv) + static_cast<int64_t>(head) * KW * a.d_h;
-  const int pairs_d = (a.d_h + 1) / 2;
   for (int d0 = 0; d0 < pairs_d; d0 += kThreads) {
     const int span = min(kThreads, pairs_d - d0);
     const int split = max(1, kThreads / span);
@@ -162,20 +201,36 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     if (part < split) {
       const int e0 = static_cast<int>((static_cast<int64_t>(part) * KW) / split);
       const int e1 = static_cast<int>((static_cast<int64_t>(part + 1) * KW) / split);
-#pragma unroll 8
-      for (int e = e0; e < e1; ++e) {
-        const float w0 = load_elem(wuv, static_cast<int64_t>(e) * a.d_h + d);
-        const float w1 = two ? load_elem(wuv, static_cast<int64_t>(e) * a.d_h + d + 1) : 0.f;
-        const float4 o0 = *reinterpret_cast<const float4*>(ot + e * kBatchGroup);
-        const float4 o1 = *reinterpret_cast<const float4*>(ot + e * kBatchGroup + 4);
-        acc0[0] += w0 * o0.x; acc1[0] += w1 * o0.x;
-        acc0[1] += w0 * o0.y; acc1[1] += w1 * o0.y;
-        acc0[2] += w0 * o0.z; acc1[2] += w1 * o0.z;
-        acc0[3] += w0 * o0.w; acc1[3] += w1 * o0.w;
-        acc0[4] += w0 * o1.x; acc1[4] += w1 * o1.x;
-        acc0[5] += w0 * o1.y; acc1[5] += w1 * o1.y;
-        acc0[6] += w0 * o1.z; acc1[6] += w1 * o1.z;
-        acc0[7] += w0 * o1.w; acc1[7] += w1 * o1.w;
+      const int db = two ? d + 1 : d;
+      for (int e = e0; e < e1; e += kWPrefetch) {
+        float2 wl[kWPrefetch];
+        if (d0 == 0 && e == e0) {
+#pragma unroll
+          for (int u = 0; u < kWPrefetch; ++u) wl[u] = wpre[u];
+        } else {
+#pragma unroll
+          for (int u = 0; u < kWPrefetch; ++u) {
+            const int ee = min(e + u, KW - 1);
+            wl[u] = load_pair<TW, EVEN>(wuv, static_cast<int64_t>(ee) * a.d_h + d,
+                                        static_cast<int64_t>(ee) * a.d_h + db);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kWPrefetch; ++u) {
+          if (e + u < e1) {
+            const float2 wv = wl[u];
+            const float4 o0 = *reinterpret_cast<const float4*>(ot + (e + u) * kBatchGroup);
+            const float4 o1 = *reinterpret_cast<const float4*>(ot + (e + u) * kBatchGroup + 4);
+            acc0[0] += wv.x * o0.x; acc1[0] += wv.y * o0.x;
+            acc0[1] += wv.x * o0.y; acc1[1] += wv.y * o0.y;
+            acc0[2] += wv.x * o0.z; acc1[2] += wv.y * o0.z;
+            acc0[3] += wv.x * o0.w; acc1[3] += wv.y * o0.w;
+            acc0[4] += wv.x * o1.x; acc1[4] += wv.y * o1.x;
+            acc0[5] += wv.x * o1.y; acc1[5] += wv.y * o1.y;
+            acc0[6] += wv.x * o1.z; acc1[6] += wv.y * o1.z;
+            acc0[7] += wv.x * o1.w; acc1[7] += wv.y * o1.w;
+          }
+        }
       }
     }
 #pragma unroll
@@ -204,12 +259,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
   const dim3 grid(a.n_heads, (a.batch + kBatchGroup - 1) / kBatchGroup);
-  const size_t sh = sizeof(float) * (kBatchGroup * a.k * a.w + kThreads * 2 * kBatchGroup +
-                                     2 * kBatchGroup * a.k);
-  if (dtype == 1)
-    combine_kernel<uint16_t><<<grid, kThreads, sh, stream>>>(a);
-  else
-    combine_kernel<float><<<grid, kThreads, sh, stream>>>(a);
+  const size_t sh = sizeof(float) * (kBatchGroup * a.k * a.w + kThreads * 2 * kBatchGroup);
+  const bool even = a.d_h % 2 == 0;
+  if (dtype == 1) {
+    if (even) combine_kernel<uint16_t, true><<<grid, kThreads, sh, stream>>>(a);
+    else combine_kernel<uint16_t, false><<<grid, kThreads, sh, stream>>>(a);
+  } else {
+    if (even) combine_kernel<float, true><<<grid, kThreads, sh, stream>>>(a);
+    else combine_kernel<float, false><<<grid, kThreads, sh, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ namespace mlra {
 //   qext         [batch][hk][w + d_r]  absorbed queries (bf16 or fp32), base-2 scaled
 //   pm, pl       fp32 [slots][hk]      partial running max / sum
 //   po           fp32 [slots][hk][w]   partial weighted latent sums
-// hk = n_heads * blocks_per_head; slots = (units + batch) * groups.
+// hk = n_heads * blocks_per_head; slots = (units + batch) * groups + 1 (the
+// last slot is kept empty: m = -inf, l = 0, o~ = 0).
 struct WsHeader {
   uint32_t magic;
   uint32_t flags;
@@ -52,6 +53,7 @@ struct DecodeArgs {
   int32_t units;
   int32_t tile_tokens;
   int32_t groups;
+  int32_t empty_slot;  // partial slot kept empty (m = -inf, l = 0, o~ = 0) for the combine
   float qscale;       // softmax_scale * log2(e)
   float out_scale;
 };
@@ -74,6 +76,7 @@ struct CombineArgs {
   float* lse;
   int64_t off_cum, off_pm, off_pl, off_po;
   int32_t batch, n_heads, d_h, w, k, hk;
+  int32_t empty_slot;  // partial slot that always reads as empty (m = -inf, l = 0, o~ = 0)
   float out_scale;
 };
 
