@@ -36,6 +36,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8K, 1 GPU"
 KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_mfma_mlra4_b32_ctx8k_counters.txt")
+COPY_BYTES = 1 << 30
 
 
 def _args():
@@ -47,7 +48,23 @@ def _args():
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy (known bytes), to scale HBM counters")
     return p.parse_args()
+
+
+def _copy_calibration(steps: int):
+    """A plain copy kernel of known size: reads and writes COPY_BYTES per launch.
+    Profiling it with the same counters as the attention kernel gives the factor
+    that turns FETCH_SIZE / WRITE_SIZE readings into bytes."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": COPY_BYTES, "launches": steps}), flush=True)
 
 
 def _source_hash() -> str:
@@ -77,8 +94,12 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the decode path "
-              "has no multi-GPU component; see the sharding notes in DESIGN.md.", file=sys.stderr)
+              "has no multi-GPU component.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        _copy_calibration(args.steps)
+        return
 
     import numpy as np
     import torch

@@ -148,8 +148,10 @@ int mlra_decode(const mlra_desc* desc, const void* pool, const int32_t* page_tab
 int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, const void* w_uv,
                  float* out, float* lse, void* stream);
 
-/* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host) and
- * clears them. Synchronises `stream`. */
+/* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host memory),
+ * after the work already enqueued on `stream` (synchronises it). The flags are
+ * reset by mlra_absorb_query / mlra_decode at the start of each step and raised
+ * by the kernels of that step; reading does not clear them. */
 int mlra_read_flags(const void* workspace, size_t ws_bytes, uint32_t* flags, void* stream);
 
 /* Text for a status code. Never NULL. */
