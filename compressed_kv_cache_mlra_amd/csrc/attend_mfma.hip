@@ -127,6 +127,12 @@ __device__ __forceinline__ float sum_4lanes(float v) {
 // lgkmcnt before any LDS result can be used).
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 __device__ __forceinline__ u32x4_t gload16(const uint8_t* p) { return *(const gu32x4_t*)(p); }
+// The same load marked nontemporal, for the cache stream: every cache row is
+// read once per step, and the streaming hint lets HBM reads run measurably
+// closer to peak than plain loads do.
+__device__ __forceinline__ u32x4_t gload16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load((const gu32x4_t*)(p));
+}
 
 __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(Decode
       for (int k = 0; k < C::NL; ++k) {
         const int p = k * C::NLT + tid;
         const int r = p / C::CPR, lc = p % C::CPR;
-        ring[k] = gload16(base + r * C::ROWB + 16 * lc);
+        ring[k] = gload16_stream(base + r * C::ROWB + 16 * lc);
       }
     } else {
       // tile spans npt pages (tok0 is page aligned): per-lane page select
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(Decode
         int32_t phys = ph[0];
 #pragma unroll
         for (int q = 1; q < C::MAXPG; ++q) phys = j == q ? ph[q] : phys;
-        ring[k] = gload16(pool + (static_cast<int64_t>(phys) * P + (r & (P - 1))) * C::ROWB + 16 * lc);
+        ring[k] = gload16_stream(pool + (static_cast<int64_t>(phys) * P + (r & (P - 1))) * C::ROWB + 16 * lc);
       }
     }
   };
