@@ -15,38 +15,64 @@ namespace {
 constexpr int kAbsorbThreads = 256;
 constexpr int kAbsorbBatchGroup = 8;
 
-// Work plan, written by one workgroup: clamped lengths, tiles per sequence
-// and their exclusive prefix sum, and the workspace header.
-__device__ void write_plan(const DecodeArgs& a, const int32_t* seq_lens) {
-  __shared__ int32_t scan_sh[kAbsorbThreads];
+// Work plan. The absorb grid has one extra row of workgroups; the first of
+// them plans while the others absorb, so planning runs beside the absorption
+// rather than before it: clamped lengths, tiles per sequence and their prefix
+// sum (built in LDS), each sequence's unit range, the empty partial slot and
+// the workspace header.
+__device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
+  __shared__ int32_t cum_sh[kMaxBatch + 1];
+  __shared__ int32_t len_sh[kMaxBatch];
+  __shared__ int32_t part_sh[kAbsorbThreads];
   const int tid = threadIdx.x;
-  int32_t* cum = reinterpret_cast<int32_t*>(a.ws + a.off_cum);
-  int32_t* nlen = reinterpret_cast<int32_t*>(a.ws + a.off_nlen);
   const int32_t cap = a.max_pages * a.page_size;
-  int32_t carry = 0;
-  for (int base = 0; base < a.batch; base += kAbsorbThreads) {
-    const int b = base + tid;
-    int32_t tiles = 0;
-    if (b < a.batch) {
-      int32_t n = seq_lens[b];
-      n = n < 0 ? 0 : (n > cap ? cap : n);
-      nlen[b] = n;
-      tiles = (n + a.tile_tokens - 1) / a.tile_tokens;
-    }
-    scan_sh[tid] = tiles;
+  const int TT = a.tile_tokens;
+  // tiles per sequence -> exclusive prefix sum; thread t scans a contiguous run
+  const int per = (a.batch + kAbsorbThreads - 1) / kAbsorbThreads;
+  const int bb = min(a.batch, tid * per), be = min(a.batch, bb + per);
+  int32_t run = 0;
+  for (int b = bb; b < be; ++b) {
+    int32_t n = seq_lens[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    len_sh[b] = n;
+    run += (n + TT - 1) / TT;
+  }
+  part_sh[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kAbsorbThreads; off <<= 1) {
+    const int32_t v = tid >= off ? part_sh[tid - off] : 0;
     __syncthreads();
-    for (int off = 1; off < kAbsorbThreads; off <<= 1) {
-      const int32_t v = tid >= off ? scan_sh[tid - off] : 0;
-      __syncthreads();
-      scan_sh[tid] += v;
-      __syncthreads();
-    }
-    if (b < a.batch) cum[b] = carry + scan_sh[tid] - tiles;
-    carry += scan_sh[kAbsorbThreads - 1];
+    part_sh[tid] += v;
     __syncthreads();
   }
-  // the empty partial slot read by the combine for slots no unit wrote
-  {
+  run = part_sh[tid] - run;
+  for (int b = bb; b < be; ++b) {
+    cum_sh[b] = run;
+    run += (len_sh[b] + TT - 1) / TT;
+  }
+  if (tid == kAbsorbThreads - 1) cum_sh[a.batch] = part_sh[kAbsorbThreads - 1];
+  __syncthreads();
+  const int32_t NT = cum_sh[a.batch];
+
+  {  // in global memory for the attention and the combine
+    int32_t* cum = reinterpret_cast<int32_t*>(a.ws + a.off_cum);
+    int32_t* nlen = reinterpret_cast<int32_t*>(a.ws + a.off_nlen);
+    int32_t* sunit = reinterpret_cast<int32_t*>(a.ws + a.off_sunit);
+    for (int b = tid; b <= a.batch; b += kAbsorbThreads) cum[b] = cum_sh[b];
+    for (int b = tid; b < a.batch; b += kAbsorbThreads) {
+      nlen[b] = len_sh[b];
+      // first and last unit whose tile range meets the sequence (last < first:
+      // no tiles), so the combine finds its partial slots with one load
+      const int32_t xa = cum_sh[b], xb = cum_sh[b + 1];
+      int32_t u0 = 0, u1 = -1;
+      if (xa < xb) {
+        u0 = unit_of_tile(xa, NT, a.units);
+        u1 = unit_of_tile(xb - 1, NT, a.units);
+      }
+      sunit[2 * b] = u0;
+      sunit[2 * b + 1] = u1;
+    }
+    // the empty partial slot read by the combine for slots no unit wrote
     const int hk_all = a.n_heads * a.k;
     float* pm = reinterpret_cast<float*>(a.ws + a.off_pm) + static_cast<int64_t>(a.empty_slot) * hk_all;
     float* pl = reinterpret_cast<float*>(a.ws + a.off_pl) + static_cast<int64_t>(a.empty_slot) * hk_all;
@@ -56,23 +82,22 @@ __device__ void write_plan(const DecodeArgs& a, const int32_t* seq_lens) {
       pl[i] = 0.f;
     }
     for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
-  }
-  if (tid == 0) {
-    cum[a.batch] = carry;
-    WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);
-    h->magic = kWsMagic;
-    h->flags = 0;
-    h->n_tiles = carry;
-    h->units = a.units;
-    h->tile_tokens = a.tile_tokens;
-    h->groups = a.groups;
-    h->batch = a.batch;
-    h->hk = a.n_heads * a.k;
+    if (tid == 0) {
+      WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);
+      h->magic = kWsMagic;
+      h->flags = 0;
+      h->n_tiles = NT;
+      h->units = a.units;
+      h->tile_tokens = a.tile_tokens;
+      h->groups = a.groups;
+      h->batch = a.batch;
+      h->hk = a.n_heads * a.k;
+    }
   }
 }
 
-// grid: (hk, ceil(batch / kAbsorbBatchGroup)); block: kAbsorbThreads.
-// Block (0, 0) also writes the work plan into the workspace header.
+// grid: (hk, ceil(batch / kAbsorbBatchGroup) + 1); block: kAbsorbThreads.
+// Block (0, last row) writes the work plan; the rest of the last row is idle.
 template <typename TIn, typename TQ>
 __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, const int32_t* seq_lens,
                                                                  const TIn* __restrict__ q_c,
@@ -87,7 +112,10 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
   const int HK = a.n_heads * a.k;
   const int QW = a.w + a.d_r;
 
-  if (blockIdx.x == 0 && blockIdx.y == 0) write_plan(a, seq_lens);
+  if (blockIdx.y == gridDim.y - 1) {  // the plan row: one workgroup plans
+    if (blockIdx.x == 0) plan_block(a, seq_lens);
+    return;
+  }
 
   for (int e = tid; e < nb * a.d_h; e += kAbsorbThreads) {
     const int bl = e / a.d_h, d = e % a.d_h;
@@ -127,7 +155,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // bf16 absorption on MFMA: for head-block pair hk and a 16-sequence tile,
 //   D[c][b] = sum_d W^UK[hk][c][d] q^C[b][head][d]   (v_mfma_f32_16x16x32_bf16)
 // with W^UK rows as the A operand and queries as the B operand, both read
-// straight from global memory 16 bytes per lane. grid: (hk, ceil(batch / 16)).
+// straight from global memory 16 bytes per lane. grid: (hk, ceil(batch / 16) + 1),
+// the last row being the plan row.
 __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs a, const int32_t* seq_lens,
                                                                       const uint16_t* __restrict__ q_c,
                                                                       const uint16_t* __restrict__ q_r,
@@ -138,7 +167,10 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
   const int b0 = blockIdx.y * 16;
   const int HK = a.n_heads * a.k;
   const int QW = a.w + a.d_r;
-  if (blockIdx.x == 0 && blockIdx.y == 0) write_plan(a, seq_lens);
+  if (blockIdx.y == gridDim.y - 1) {  // the plan row: one workgroup plans
+    if (blockIdx.x == 0) plan_block(a, seq_lens);
+    return;
+  }
 
   const int m16 = lane & 15, g4 = lane >> 4;
   const int b = b0 + m16;
@@ -182,11 +214,12 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
 
 hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int32_t* seq_lens,
                          const void* q_c, const void* q_r, const void* w_uk, hipStream_t stream) {
-  const dim3 grid(a.n_heads * a.k, (a.batch + kAbsorbBatchGroup - 1) / kAbsorbBatchGroup);
+  // the last row of every absorb grid is the plan row
+  const dim3 grid(a.n_heads * a.k, (a.batch + kAbsorbBatchGroup - 1) / kAbsorbBatchGroup + 1);
   const size_t sh = sizeof(float) * kAbsorbBatchGroup * a.d_h;
   if (dtype == 1) {
     if (q_bf16 && a.d_h % 8 == 0 && a.w % 16 == 0)
-      absorb_mfma_kernel<<<dim3(a.n_heads * a.k, (a.batch + 15) / 16), kAbsorbThreads, 0, stream>>>(
+      absorb_mfma_kernel<<<dim3(a.n_heads * a.k, (a.batch + 15) / 16 + 1), kAbsorbThreads, 0, stream>>>(
           a, seq_lens, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
           static_cast<const uint16_t*>(w_uk));
     else if (q_bf16)

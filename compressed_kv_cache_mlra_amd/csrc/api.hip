@@ -1,6 +1,7 @@
 // C ABI of libmlra: argument validation, work planning, workspace layout and
 // kernel launches. The public contract is documented in include/mlra.h.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "../../include/mlra.h"
@@ -30,7 +31,7 @@ struct Plan {
   int groups;
   int units;
   int64_t slots;
-  size_t off_cum, off_nlen, off_qext, off_pm, off_pl, off_po, total;
+  size_t off_cum, off_nlen, off_sunit, off_qext, off_pm, off_pl, off_po, total;
   bool q_bf16;
 };
 
@@ -57,6 +58,8 @@ int make_plan(const mlra_desc* d, Plan* p) {
   off = align_up(off + sizeof(int32_t) * (d->batch + 1));
   p->off_nlen = off;
   off = align_up(off + sizeof(int32_t) * d->batch);
+  p->off_sunit = off;
+  off = align_up(off + sizeof(int32_t) * 2 * d->batch);
   p->off_qext = off;
   off = align_up(off + qelem * static_cast<size_t>(d->batch) * s.hk * (s.w + d->d_r));
   p->off_pm = off;
@@ -78,6 +81,7 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.ws = static_cast<char*>(ws);
   a.off_cum = static_cast<int64_t>(p.off_cum);
   a.off_nlen = static_cast<int64_t>(p.off_nlen);
+  a.off_sunit = static_cast<int64_t>(p.off_sunit);
   a.off_qext = static_cast<int64_t>(p.off_qext);
   a.off_pm = static_cast<int64_t>(p.off_pm);
   a.off_pl = static_cast<int64_t>(p.off_pl);
@@ -194,7 +198,7 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   c.w_uv = w_uv;
   c.out = out;
   c.lse = lse;
-  c.off_cum = static_cast<int64_t>(p.off_cum);
+  c.off_sunit = static_cast<int64_t>(p.off_sunit);
   c.off_pm = static_cast<int64_t>(p.off_pm);
   c.off_pl = static_cast<int64_t>(p.off_pl);
   c.off_po = static_cast<int64_t>(p.off_po);
@@ -204,6 +208,7 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   c.w = p.s.w;
   c.k = desc->blocks_per_head;
   c.hk = p.s.hk;
+  c.groups = p.groups;
   c.empty_slot = static_cast<int32_t>(p.slots - 1);
   c.out_scale = desc->out_scale > 0.f ? desc->out_scale
                                       : 1.0f / sqrtf(static_cast<float>(desc->blocks_per_head));

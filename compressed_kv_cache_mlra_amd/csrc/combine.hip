@@ -59,7 +59,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   extern __shared__ float sh[];
   float* ot = sh;                             // [k * w][kBatchGroup]
   float* red = sh + kBatchGroup * a.k * a.w;  // [kThreads][2 * kBatchGroup]
-  __shared__ int32_t sinfo[kBatchGroup][2];   // per sequence: first, last unit (last < first: empty)
 
   const int tid = threadIdx.x;
   const int head = blockIdx.x;
@@ -77,7 +76,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int part0 = tid / span0;
   const int d_0 = 2 * (tid % span0);
   const int e0_0 = static_cast<int>((static_cast<int64_t>(part0) * KW) / split0);
-  const int e1_0 = static_cast<int>((static_cast<int64_t>(part0 + 1) * KW) / split0);
   const int d_0b = min(d_0 + 1, a.d_h - 1);
   float2 wpre[kWPrefetch];
 #pragma unroll
@@ -92,27 +90,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t NT = *(cint32_t*)(&hdr->n_tiles), units = *(cint32_t*)(&hdr->units);
   const int32_t G = *(cint32_t*)(&hdr->groups);
-  const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
+  const int32_t* sunit = reinterpret_cast<const int32_t*>(a.ws + a.off_sunit);
   const float* pm = reinterpret_cast<const float*>(a.ws + a.off_pm);
   const float* pl = reinterpret_cast<const float*>(a.ws + a.off_pl);
   const float* po = reinterpret_cast<const float*>(a.ws + a.off_po);
   const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;  // first entry of the empty slot
 
-  if (tid == 0) {
-    for (int bl = 0; bl < kBatchGroup; ++bl) {
-      int32_t u0 = 0, u1 = -1;
-      if (bl < nb) {
-        const int32_t xa = *(cint32_t*)(cum + b0 + bl), xb = *(cint32_t*)(cum + b0 + bl + 1);
-        if (xa < xb) {
-          u0 = unit_of_tile(xa, NT, units);
-          u1 = unit_of_tile(xb - 1, NT, units);
-        }
-      }
-      sinfo[bl][0] = u0;
-      sinfo[bl][1] = u1;
-    }
-  }
-  __syncthreads();
 
   // ---- merge: item = (pair, 4 columns); 16 slots of loads in flight per batch
   const int w4 = a.w / 4;
@@ -125,8 +108,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       const int p = it / w4, c = 4 * (it % w4);
       const int bl = p / a.k, jj = p % a.k;
       const int b = b0 + bl, hk = head * a.k + jj;
-      const int32_t u0 = sinfo[bl][0];
-      const int nslots = (sinfo[bl][1] - u0 + 1) * G;
+      const int2 su = *reinterpret_cast<const int2*>(sunit + 2 * b);  // first, last unit
+      const int32_t u0 = su.x;
+      const int nslots = (su.y - u0 + 1) * G;
       float M = -INFINITY, L = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s0 = 0; s0 < nslots; s0 += kSlotBatch) {
@@ -255,9 +239,226 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Combine for bf16 W^UV with d_h = 128 and compile-time block width / blocks
+// per head: the shapes the MFMA attention runs. Same arithmetic as
+// combine_kernel; the work is laid out so that a workgroup needs two dependent
+// memory round trips (unit ranges, then all partial slots at once):
+//   * one workgroup per (head, 4 sequences), 256 threads;
+//   * merge: item = (sequence, 4 latent columns, half); the two halves of an
+//     item take alternate partial slots (up to kFastSlots each per batch) and
+//     are merged with one lane exchange;
+//   * product: thread = (8 output columns, row residue r mod 16); its W^UV
+//     rows are requested with 16-byte loads before the merge starts; the 16
+//     row residues are summed with lane swaps inside a wave and through LDS
+//     across the four waves.
+constexpr int kFastThreads = 256;
+constexpr int kFastSeq = 4;     // sequences per workgroup
+constexpr int kFastSlots = 12;  // partial slots per half whose loads are in flight together
+constexpr int kFastDh = 128;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float sum_lanes_16_32_48(float v) {
+  // sum over lanes l, l^16, l^32, l^48
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int W, int KB>
+__global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs a) {
+  constexpr int K = W * KB;               // merged latent columns per head
+  constexpr int CG = K / 4;               // 4-column groups per sequence
+  constexpr int NITEMS = kFastSeq * CG * 2;
+  static_assert(NITEMS % kFastThreads == 0, "merge items must fill the workgroup");
+  constexpr int ROWS = K / 16;            // W^UV rows per thread
+  constexpr int RB = ROWS < 16 ? ROWS : 16;  // rows per load batch
+  __shared__ __attribute__((aligned(16))) float ot[K][kFastSeq];        // merged latents, transposed
+  __shared__ __attribute__((aligned(16))) float red[4][16][8][kFastSeq];  // per-wave partial outputs
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.x;
+  const int b0 = blockIdx.y * kFastSeq;
+  const int nb = min(kFastSeq, a.batch - b0);
+
+  // ---- W^UV rows of this thread: e = rr + 16 i, columns [8 dc, 8 dc + 8)
+  const int dc = tid & 15, rr = tid >> 4;
+  const uint16_t* wuv = static_cast<const uint16_t*>(a.w_uv) + static_cast<int64_t>(head) * K * kFastDh + 8 * dc;
+  typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+  u32x4_t wr[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) wr[i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * i) * kFastDh);
+
+  typedef __attribute__((address_space(4))) const int32_t cint32_t;
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t NT = *(cint32_t*)(&hdr->n_tiles), units = *(cint32_t*)(&hdr->units);
+  const int32_t G = a.groups;
+  const int32_t* sunit = reinterpret_cast<const int32_t*>(a.ws + a.off_sunit);
+  const float* pm = reinterpret_cast<const float*>(a.ws + a.off_pm);
+  const float* pl = reinterpret_cast<const float*>(a.ws + a.off_pl);
+  const float* po = reinterpret_cast<const float*>(a.ws + a.off_po);
+  const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;
+
+  // ---- merge
+  auto merge = [&](auto check_units) __attribute__((always_inline)) {
+    constexpr bool kCheck = decltype(check_units)::value;
+#pragma unroll
+    for (int it0 = 0; it0 < NITEMS; it0 += kFastThreads) {
+      const int it = it0 + tid;
+      const int half = it & 1;
+      const int cgi = (it >> 1) % CG, bl = (it >> 1) / CG;
+      const int e = 4 * cgi, jj = e / W, c = e % W;
+      const int b = min(b0 + bl, a.batch - 1);  // rows past the batch merge a real sequence, unused
+      const int hk = head * KB + jj;
+      const int2 su = *reinterpret_cast<const int2*>(sunit + 2 * b);  // first, last unit
+      const int nslots = (su.y - su.x + 1) * G;
+      float M = -INFINITY, L = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s0 = half; s0 < nslots; s0 += 2 * kFastSlots) {
+        float ms[kFastSlots], ls[kFastSlots];
+        float4 vs[kFastSlots];
+#pragma unroll
+        for (int u = 0; u < kFastSlots; ++u) {
+          const int sl = s0 + 2 * u;
+          const int32_t uu = su.x + sl / G;
+          const bool ok = sl < nslots && (!kCheck || unit_owns_tiles(uu, NT, units));
+          const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + sl % G) * a.hk + hk : empty_hk + hk;
+          ms[u] = pm[idx];
+          ls[u] = pl[idx];
+          vs[u] = *reinterpret_cast<const float4*>(po + idx * W + c);
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kFastSlots; ++u) mb = fmaxf(mb, ms[u]);
+        const float mu = mb == -INFINITY ? 0.f : mb;
+        const float r = fast_exp2(M - mu);
+        L *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+#pragma unroll
+        for (int u = 0; u < kFastSlots; ++u) {
+          const float wgt = fast_exp2(ms[u] - mu);  // 0 for empty slots (m = -inf)
+          L += wgt * ls[u];
+          acc.x += wgt * vs[u].x;
+          acc.y += wgt * vs[u].y;
+          acc.z += wgt * vs[u].z;
+          acc.w += wgt * vs[u].w;
+        }
+        M = mb;
+      }
+      // merge the two halves (lanes 2q and 2q+1)
+      const float Mo = __shfl_xor(M, 1), Lo = __shfl_xor(L, 1);
+      const float4 ao = make_float4(__shfl_xor(acc.x, 1), __shfl_xor(acc.y, 1), __shfl_xor(acc.z, 1),
+                                    __shfl_xor(acc.w, 1));
+      const float Mt = fmaxf(M, Mo);
+      const float mu = Mt == -INFINITY ? 0.f : Mt;
+      const float r0 = fast_exp2(M - mu), r1 = fast_exp2(Mo - mu);
+      const float Lt = L * r0 + Lo * r1;
+      const float invL = nslots > 0 ? 1.f / Lt : 0.f;
+      if (half == 0) {
+        if (c == 0 && a.lse && bl < nb)
+          a.lse[(static_cast<int64_t>(b) * a.n_heads + head) * KB + jj] =
+              nslots > 0 ? 0.69314718055994531f * (Mt + __log2f(Lt)) : -INFINITY;
+        ot[e + 0][bl] = (acc.x * r0 + ao.x * r1) * invL;
+        ot[e + 1][bl] = (acc.y * r0 + ao.y * r1) * invL;
+        ot[e + 2][bl] = (acc.z * r0 + ao.z * r1) * invL;
+        ot[e + 3][bl] = (acc.w * r0 + ao.w * r1) * invL;
+      }
+    }
+  };
+  if (NT >= units)
+    merge(std::false_type{});
+  else
+    merge(std::true_type{});
+  __syncthreads();
+
+  // ---- product: acc[j][bl] = sum over this thread's rows of W^UV[e][8 dc + j] o~[bl][e]
+  float acc[8][kFastSeq];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int bl = 0; bl < kFastSeq; ++bl) acc[j][bl] = 0.f;
+#pragma unroll
+  for (int i0 = 0; i0 < ROWS; i0 += RB) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        wr[i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * (i0 + i)) * kFastDh);
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int e = rr + 16 * (i0 + i);
+      const float4 o = *reinterpret_cast<const float4*>(&ot[e][0]);
+      const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t u = wr[i][q];
+        const float wlo = __uint_as_float(u << 16), whi = __uint_as_float(u & 0xffff0000u);
+#pragma unroll
+        for (int bl = 0; bl < kFastSeq; ++bl) {
+          acc[2 * q][bl] += wlo * ov[bl];
+          acc[2 * q + 1][bl] += whi * ov[bl];
+        }
+      }
+    }
+  }
+  // the wave's four row residues (lanes l, l^16, l^32, l^48) hold the same columns
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int bl = 0; bl < kFastSeq; ++bl) acc[j][bl] = sum_lanes_16_32_48(acc[j][bl]);
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<float4*>(&red[wave][dc][j][0]) =
+          make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  }
+  __syncthreads();
+  // outputs: f = (bl, d), d fastest
+#pragma unroll
+  for (int f0 = 0; f0 < kFastSeq * kFastDh; f0 += kFastThreads) {
+    const int f = f0 + tid;
+    const int bl = f / kFastDh, d = f % kFastDh;
+    if (bl < nb) {
+      const float v = red[0][d >> 3][d & 7][bl] + red[1][d >> 3][d & 7][bl] + red[2][d >> 3][d & 7][bl] +
+                      red[3][d >> 3][d & 7][bl];
+      a.out[(static_cast<int64_t>(b0 + bl) * a.n_heads + head) * kFastDh + d] = a.out_scale * v;
+    }
+  }
+}
+
+template <int W, int KB>
+void launch_fast(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(a.n_heads, (a.batch + kFastSeq - 1) / kFastSeq);
+  combine_fast_kernel<W, KB><<<grid, kFastThreads, 0, stream>>>(a);
+}
+
+// Runs the specialised combine when the shape has one; false otherwise.
+bool try_launch_fast(const CombineArgs& a, int dtype, hipStream_t stream) {
+  if (dtype != 1 || a.d_h != kFastDh) return false;
+  switch (a.w * 8 + a.k) {
+    case 128 * 8 + 1: launch_fast<128, 1>(a, stream); return true;
+    case 128 * 8 + 2: launch_fast<128, 2>(a, stream); return true;
+    case 128 * 8 + 4: launch_fast<128, 4>(a, stream); return true;
+    case 256 * 8 + 1: launch_fast<256, 1>(a, stream); return true;
+    case 256 * 8 + 2: launch_fast<256, 2>(a, stream); return true;
+    case 256 * 8 + 4: launch_fast<256, 4>(a, stream); return true;
+    case 512 * 8 + 1: launch_fast<512, 1>(a, stream); return true;
+    case 512 * 8 + 2: launch_fast<512, 2>(a, stream); return true;
+    default: return false;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
+  if (try_launch_fast(a, dtype, stream)) return hipGetLastError();
   const dim3 grid(a.n_heads, (a.batch + kBatchGroup - 1) / kBatchGroup);
   const size_t sh = sizeof(float) * (kBatchGroup * a.k * a.w + kThreads * 2 * kBatchGroup);
   const bool even = a.d_h % 2 == 0;

@@ -30,13 +30,14 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 constexpr uint32_t kWsMagic = 0x4d4c5241u;  // "MLRA"
 constexpr uint32_t kFlagBadPage = 1u;       // same value as MLRA_FLAG_BAD_PAGE
+constexpr int kMaxBatch = 4096;             // sequences per call (the plan keeps them in LDS)
 
 // Everything a decode kernel needs, passed by value.
 struct DecodeArgs {
   const void* pool;
   const int32_t* page_table;  // nullptr: identity layout
   char* ws;
-  int64_t off_cum, off_nlen, off_qext, off_pm, off_pl, off_po;
+  int64_t off_cum, off_nlen, off_sunit, off_qext, off_pm, off_pl, off_po;
   int32_t batch;
   int32_t n_heads;
   int32_t d_h;
@@ -74,8 +75,9 @@ struct CombineArgs {
   const void* w_uv;
   float* out;
   float* lse;
-  int64_t off_cum, off_pm, off_pl, off_po;
+  int64_t off_sunit, off_pm, off_pl, off_po;
   int32_t batch, n_heads, d_h, w, k, hk;
+  int32_t groups;      // head groups per work unit (partial slots per unit and sequence)
   int32_t empty_slot;  // partial slot that always reads as empty (m = -inf, l = 0, o~ = 0)
   float out_scale;
 };

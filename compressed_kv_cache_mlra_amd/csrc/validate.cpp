@@ -1,6 +1,8 @@
 // Host-side descriptor validation of libmlra.
 #include "validate.h"
 
+#include "common.h"
+
 #include <math.h>
 #include <stdint.h>
 
@@ -30,6 +32,7 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
       isinf(d->softmax_scale) || isinf(d->out_scale))
     return MLRA_ERR_INVALID_ARG;
   // Kernel limits of this build.
+  if (d->batch > kMaxBatch) return MLRA_ERR_UNSUPPORTED;
   if (d->d_h > 512 || d->d_r > 512 || w > 512) return MLRA_ERR_UNSUPPORTED;
   if (d->blocks_per_head * w > 1024 || d->blocks_per_head > 32) return MLRA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->n_heads) * d->blocks_per_head > 65535) return MLRA_ERR_UNSUPPORTED;

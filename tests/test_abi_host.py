@@ -66,6 +66,7 @@ BAD_DESCS = [
     (dict(num_pages=0), mlra.ERR_INVALID_ARG),
     (dict(d_r=-8), mlra.ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), mlra.ERR_INVALID_ARG),
+    (dict(batch=4097), mlra.ERR_UNSUPPORTED),          # the plan keeps the batch in LDS
 ]
 
 
@@ -142,3 +143,19 @@ def test_binding_rejects_cpu_tensors():
     d = _desc()
     with pytest.raises(ValueError):
         mlra.attend(d, torch.zeros(10), None, torch.zeros(10, dtype=torch.uint8))
+
+
+
+def test_absorb_query_validation():
+    """The planning call validates like the others before launching."""
+    L = mlra.lib()
+    d = _desc()
+    need = mlra.workspace_bytes(d, 100)
+    absorb = L.mlra_absorb_query
+    assert absorb(None, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(need), None) == mlra.ERR_INVALID_ARG
+    for i in (1, 2, 4, 5):  # seq_lens, q_c, w_uk, workspace
+        args = [ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(need), None]
+        args[i] = None
+        assert absorb(*args) == mlra.ERR_INVALID_ARG, i
+    assert absorb(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(need - 1), None) == \
+        mlra.ERR_WORKSPACE
