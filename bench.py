@@ -179,10 +179,54 @@ def main():
     pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attend_ms = [e[1].elapsed_time(e[2]) for e in evs]
     comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ev_ms = [e[0].elapsed_time(e[3]) for e in evs]
 
+    # The same K steps replayed from HIP graphs (one graph per pool instance).
+    graphs = []
+    for p in range(len(pools)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            gstep_pool = pools[p]
+            if append:
+                mlra.append_latent(desc, gstep_pool, page_table, positions, x, w_dkv, kr_new, None, cs)
+            mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
+            mlra.attend(desc, gstep_pool, page_table, ws, cs)
+            mlra.combine(desc, ws, w_uv, out, None, cs)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms_per_step = g0.elapsed_time(g1) / args.steps
+    del graphs
+
+    # Reference: a plain streaming read of as many bytes as the attention's
+    # algorithmic cache bytes, same loads and launch shape, rotated over as many
+    # buffers as there are pool instances.
     elem = 2 if s.dtype == "bf16" else 4
     n_tokens = int(np.sum(inp.seq_lens.astype(np.int64)))
     cache_bytes = float(n_tokens) * (s.d_c + s.d_r) * elem  # read once per step, k^R not re-read
+    rbytes = int(cache_bytes) // 16 * 16
+    rbufs = [torch.empty(rbytes, dtype=torch.uint8, device="cuda") for _ in pools]
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for i in range(args.steps):
+        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = rbytes / (r0.elapsed_time(r1) / args.steps * 1e-3) / 1e9
+    del rbufs
+
     heads_per_block = s.n_heads * s.blocks_per_head // s.n_blocks
     # per token: every (head, attended block) pair scores w + d_r and accumulates w
     attn_flops = float(n_tokens) * s.n_heads * s.blocks_per_head * (4.0 * s.w + 2.0 * s.d_r)
@@ -208,9 +252,16 @@ def main():
                    "context_tokens": n_tokens, "heads_per_block": heads_per_block,
                    "pool_instances": len(pools), "parallelism": "single GPU"},
         "cache_gbps_full_step": round(cache_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "graph_ms_per_step": round(graph_ms_per_step, 5),
+        "step_us_with_events": {"p10": round(1e3 * float(np.percentile(step_ev_ms, 10)), 2),
+                                "p50": round(1e3 * float(np.percentile(step_ev_ms, 50)), 2),
+                                "p90": round(1e3 * float(np.percentile(step_ev_ms, 90)), 2)},
+        "stream_read_gbps_same_device": round(read_gbps, 1),
+        "attend_frac_of_stream_read": round(achieved / read_gbps, 4),
         "cache_pct_of_hbm_peak_full_step": round(100.0 * cache_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "kernel_us_with_events": {"append_absorb": round(1e3 * float(np.mean(pre_ms)), 2),
                       "attend": round(1e3 * attend_mean_ms, 2),
+                      "attend_p50": round(1e3 * float(np.percentile(attend_ms, 50)), 2),
                       "attend_p10": round(1e3 * float(np.percentile(attend_ms, 10)), 2),
                       "attend_p90": round(1e3 * float(np.percentile(attend_ms, 90)), 2),
                       "combine": round(1e3 * float(np.mean(comb_ms)), 2)},

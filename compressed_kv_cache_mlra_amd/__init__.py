@@ -8,7 +8,7 @@ every call raises if the library is not built or no GPU is present.
 
 Entry points (same names as the C ABI, without the mlra_ prefix):
   workspace_bytes, append_latent, absorb_query, attend, decode, combine,
-  read_flags, status_string.
+  read_flags, status_string; and the measurement helper stream_read.
 """
 from __future__ import annotations
 
@@ -76,8 +76,9 @@ def lib() -> ctypes.CDLL:
         L.mlra_decode.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
+        L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
-                  "mlra_combine", "mlra_read_flags"):
+                  "mlra_combine", "mlra_read_flags", "mlra_stream_read"):
             getattr(L, f).restype = ctypes.c_int
         if L.mlra_abi_version() != ABI_VERSION:
             raise ImportError("libmlra ABI version mismatch; rebuild the library")
@@ -248,6 +249,17 @@ class DecodeStep:
                self.workspace, stream)
         combine(self.desc, self.workspace, w_uv, out, lse, stream)
         return out
+
+
+def stream_read(src, sink, stream=None):
+    """Measurement helper: reads all of `src` (a GPU tensor whose size in bytes
+    is a multiple of 16) once, as the attention reads the cache; `sink` is a
+    GPU tensor of at least 16 KiB that receives a checksum."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().mlra_stream_read(
+        _ptr(src, kind="bytes", name="src"), ctypes.c_size_t(nbytes),
+        _ptr(sink, kind="bytes", name="sink"), ctypes.c_size_t(sink.numel() * sink.element_size()),
+        _stream(stream)), "stream_read")
 
 
 def default_softmax_scale(desc: MlraDesc) -> float:

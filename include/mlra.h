@@ -74,7 +74,7 @@ typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1 } mlra_dtype;
 #define MLRA_FLAG_BAD_PAGE 1u
 
 typedef struct {
-  int32_t batch;             /* B, number of sequences (>= 1) */
+  int32_t batch;             /* B, number of sequences (1 .. 4096) */
   int32_t n_heads;           /* h */
   int32_t d_h;               /* query / value head width (1 .. 512) */
   int32_t d_c;               /* latent width stored in each cache row */
@@ -153,6 +153,16 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
  * reset by mlra_absorb_query / mlra_decode at the start of each step and raised
  * by the kernels of that step; reading does not clear them. */
 int mlra_read_flags(const void* workspace, size_t ws_bytes, uint32_t* flags, void* stream);
+
+/* Measurement helper, not part of the decode path: reads `bytes` (a multiple
+ * of 16) of device memory at `src` once, with the 16-byte nontemporal loads
+ * and the two-workgroups-per-compute-unit launch that mlra_attend uses for
+ * the cache, so the attention's bandwidth can be stated against a plain read
+ * on the same device. `sink` (device, >= 16 KiB suffices: 4 bytes per
+ * workgroup) receives a checksum so the reads cannot be elided.
+ * Errors: MLRA_ERR_INVALID_ARG for NULL pointers, a size not a multiple of 16
+ * or a sink that is too small. Asynchronous on `stream`. */
+int mlra_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
 /* Text for a status code. Never NULL. */
 const char* mlra_status_string(int status);

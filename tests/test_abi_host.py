@@ -159,3 +159,11 @@ def test_absorb_query_validation():
         assert absorb(*args) == mlra.ERR_INVALID_ARG, i
     assert absorb(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_size_t(need - 1), None) == \
         mlra.ERR_WORKSPACE
+
+
+def test_stream_read_validation():
+    L = mlra.lib()
+    assert L.mlra_stream_read(None, 1024, FAKE, 1 << 20, None) == mlra.ERR_INVALID_ARG
+    assert L.mlra_stream_read(FAKE, 1024, None, 1 << 20, None) == mlra.ERR_INVALID_ARG
+    assert L.mlra_stream_read(FAKE, 1000, FAKE, 1 << 20, None) == mlra.ERR_INVALID_ARG  # not a multiple of 16
+    assert L.mlra_stream_read(FAKE, 1024, FAKE, 4, None) == mlra.ERR_INVALID_ARG        # sink too small

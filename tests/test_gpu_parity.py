@@ -231,3 +231,32 @@ def test_side_stream():
     out = prob.out.cpu().numpy().astype(np.float64)
     ref, _ = oracle.decode_unabsorbed(inp)
     _gpu.check_outputs(out.reshape(-1, 128), ref, "bf16")
+
+
+def test_graph_replay_matches_eager():
+    """A decode step (absorb, attend, combine) captured in a HIP graph and
+    replayed several times, with eager work and synchronisations between the
+    replays, gives the eager result bit for bit every time (no memset nodes:
+    the plan and partials are written by kernels)."""
+    _say("case: graph replay, small MLRA-4 shape")
+    t = _gpu.torch()
+    kw, lens = SMALL[2]
+    s = synth.Shape(batch=len(lens), **kw)
+    inp = synth.make_inputs(s, ("list", lens), 4101)
+    prob = _gpu.GpuProblem(inp)
+    eager, eager_l = prob.run()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        prob.step(t.cuda.current_stream())
+    for rep in range(3):
+        prob.out.zero_()
+        prob.lse.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(prob.out.cpu().numpy().astype(np.float64), eager), rep
+        assert np.array_equal(prob.lse.cpu().numpy().astype(np.float64), eager_l), rep
+        # eager work between replays
+        junk = t.randn(1 << 20, device="cuda")
+        junk.mul_(2.0).sum().item()
+        prob.step()
+        t.cuda.synchronize()
