@@ -49,6 +49,8 @@ def _args():
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the graph-replay and streaming-read legs (for profiler runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (known bytes), to scale HBM counters")
     return p.parse_args()
@@ -181,52 +183,15 @@ def main():
     comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
     step_ev_ms = [e[0].elapsed_time(e[3]) for e in evs]
 
-    # The same K steps replayed from HIP graphs (one graph per pool instance).
-    graphs = []
-    for p in range(len(pools)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream()
-            gstep_pool = pools[p]
-            if append:
-                mlra.append_latent(desc, gstep_pool, page_table, positions, x, w_dkv, kr_new, None, cs)
-            mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
-            mlra.attend(desc, gstep_pool, page_table, ws, cs)
-            mlra.combine(desc, ws, w_uv, out, None, cs)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms_per_step = g0.elapsed_time(g1) / args.steps
-    del graphs
+    graph_ms_per_step, read_gbps = None, None
+    if not args.no_extras:
+        graph_ms_per_step, read_gbps = _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk,
+                                               w_uv, ws, desc, out, stream, append,
+                                               (positions, x, w_dkv, kr_new) if append else None,
+                                               _cache_bytes(inp, s))
 
-    # Reference: a plain streaming read of as many bytes as the attention's
-    # algorithmic cache bytes, same loads and launch shape, rotated over as many
-    # buffers as there are pool instances.
-    elem = 2 if s.dtype == "bf16" else 4
     n_tokens = int(np.sum(inp.seq_lens.astype(np.int64)))
-    cache_bytes = float(n_tokens) * (s.d_c + s.d_r) * elem  # read once per step, k^R not re-read
-    rbytes = int(cache_bytes) // 16 * 16
-    rbufs = [torch.empty(rbytes, dtype=torch.uint8, device="cuda") for _ in pools]
-    sink = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
-    for i in range(args.warmup):
-        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
-    torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for i in range(args.steps):
-        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    read_gbps = rbytes / (r0.elapsed_time(r1) / args.steps * 1e-3) / 1e9
-    del rbufs
-
+    cache_bytes = _cache_bytes(inp, s)
     heads_per_block = s.n_heads * s.blocks_per_head // s.n_blocks
     # per token: every (head, attended block) pair scores w + d_r and accumulates w
     attn_flops = float(n_tokens) * s.n_heads * s.blocks_per_head * (4.0 * s.w + 2.0 * s.d_r)
@@ -247,17 +212,17 @@ def main():
         "vs_baseline": None,
         "dtype": s.dtype,
         "data": "synthetic",
-        "config": {"workload": wl["name"], "batch": s.batch, "n_heads": s.n_heads, "d_h": s.d_h,
+        "config": {"workload": wl["name"], "workload_id": args.workload, "batch": s.batch, "n_heads": s.n_heads, "d_h": s.d_h,
                    "d_c": s.d_c, "n_blocks": s.n_blocks, "d_r": s.d_r, "page_size": s.page_size,
                    "context_tokens": n_tokens, "heads_per_block": heads_per_block,
                    "pool_instances": len(pools), "parallelism": "single GPU"},
         "cache_gbps_full_step": round(cache_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "graph_ms_per_step": round(graph_ms_per_step, 5),
+        "graph_ms_per_step": None if graph_ms_per_step is None else round(graph_ms_per_step, 5),
         "step_us_with_events": {"p10": round(1e3 * float(np.percentile(step_ev_ms, 10)), 2),
                                 "p50": round(1e3 * float(np.percentile(step_ev_ms, 50)), 2),
                                 "p90": round(1e3 * float(np.percentile(step_ev_ms, 90)), 2)},
-        "stream_read_gbps_same_device": round(read_gbps, 1),
-        "attend_frac_of_stream_read": round(achieved / read_gbps, 4),
+        "stream_read_gbps_same_device": None if read_gbps is None else round(read_gbps, 1),
+        "attend_frac_of_stream_read": None if read_gbps is None else round(achieved / read_gbps, 4),
         "cache_pct_of_hbm_peak_full_step": round(100.0 * cache_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "kernel_us_with_events": {"append_absorb": round(1e3 * float(np.mean(pre_ms)), 2),
                       "attend": round(1e3 * attend_mean_ms, 2),
@@ -273,6 +238,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes_per_launch": cache_bytes,
+            "algorithmic_flops_per_launch": attn_flops,
             "traffic": _traffic(cache_bytes),
             "mfma_tflops": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12, 2),
             "mfma_frac_of_bf16_peak": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -283,6 +249,59 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _cache_bytes(inp, s):
+    """Algorithmic cache bytes of one step: every attended token's row once
+    (k^R is read once for all blocks)."""
+    import numpy as np
+    elem = 2 if s.dtype == "bf16" else 4
+    return float(np.sum(inp.seq_lens.astype(np.int64))) * (s.d_c + s.d_r) * elem
+
+
+def _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk, w_uv, ws, desc, out, stream,
+            append, app, cache_bytes):
+    """(1) The same K steps replayed from HIP graphs, one graph per pool
+    instance; (2) a plain streaming read of as many bytes as the attention's
+    algorithmic cache bytes, with the attention's loads and launch shape,
+    rotated over as many buffers as there are pool instances."""
+    graphs = []
+    for p in range(len(pools)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            if append:
+                mlra.append_latent(desc, pools[p], page_table, *app, None, cs)
+            mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
+            mlra.attend(desc, pools[p], page_table, ws, cs)
+            mlra.combine(desc, ws, w_uv, out, None, cs)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graphs
+
+    rbytes = int(cache_bytes) // 16 * 16
+    rbufs = [torch.empty(rbytes, dtype=torch.uint8, device="cuda") for _ in pools]
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    for i in range(args.warmup):
+        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for i in range(args.steps):
+        mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = rbytes / (r0.elapsed_time(r1) / args.steps * 1e-3) / 1e9
+    return graph_ms, read_gbps
 
 
 def _cpu_baseline(inp, target_s: float):
