@@ -19,7 +19,8 @@ constexpr int kAbsorbBatchGroup = 8;
 // them plans while the others absorb, so planning runs beside the absorption
 // rather than before it: clamped lengths, tiles per sequence and their prefix
 // sum (built in LDS), each sequence's unit range, the empty partial slot and
-// the workspace header.
+// the workspace header, and one descriptor per work unit so an attention
+// workgroup learns its tile range and first sequence with one scalar fetch.
 __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
   __shared__ int32_t cum_sh[kMaxBatch + 1];
   __shared__ int32_t len_sh[kMaxBatch];
@@ -82,6 +83,19 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
       pl[i] = 0.f;
     }
     for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
+    int32_t* udesc = reinterpret_cast<int32_t*>(a.ws + a.off_udesc);
+    for (int u = tid; u < a.units; u += kAbsorbThreads) {
+      const int32_t x0 = tile_begin(u, NT, a.units), x1 = tile_begin(u + 1, NT, a.units);
+      // sequence owning tile x0: the largest b with cum_sh[b] <= x0
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cum_sh[mid] <= x0) lo = mid; else hi = mid - 1;
+      }
+      int4* dst = reinterpret_cast<int4*>(udesc + static_cast<int64_t>(u) * kUnitDescInts);
+      dst[0] = make_int4(x0, x1, lo, cum_sh[lo]);
+      dst[1] = make_int4(cum_sh[lo + 1], len_sh[lo], 0, 0);
+    }
     if (tid == 0) {
       WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);
       h->magic = kWsMagic;

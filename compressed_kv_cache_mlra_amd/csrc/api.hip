@@ -31,7 +31,7 @@ struct Plan {
   int groups;
   int units;
   int64_t slots;
-  size_t off_cum, off_nlen, off_sunit, off_qext, off_pm, off_pl, off_po, total;
+  size_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po, total;
   bool q_bf16;
 };
 
@@ -60,6 +60,8 @@ int make_plan(const mlra_desc* d, Plan* p) {
   off = align_up(off + sizeof(int32_t) * d->batch);
   p->off_sunit = off;
   off = align_up(off + sizeof(int32_t) * 2 * d->batch);
+  p->off_udesc = off;
+  off = align_up(off + sizeof(int32_t) * kUnitDescInts * static_cast<size_t>(p->units));
   p->off_qext = off;
   off = align_up(off + qelem * static_cast<size_t>(d->batch) * s.hk * (s.w + d->d_r));
   p->off_pm = off;
@@ -82,6 +84,7 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.off_cum = static_cast<int64_t>(p.off_cum);
   a.off_nlen = static_cast<int64_t>(p.off_nlen);
   a.off_sunit = static_cast<int64_t>(p.off_sunit);
+  a.off_udesc = static_cast<int64_t>(p.off_udesc);
   a.off_qext = static_cast<int64_t>(p.off_qext);
   a.off_pm = static_cast<int64_t>(p.off_pm);
   a.off_pl = static_cast<int64_t>(p.off_pl);

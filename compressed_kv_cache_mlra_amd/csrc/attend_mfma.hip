@@ -164,20 +164,16 @@ __global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(Decode
   const bool loader = tid < C::NLT;
 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
-  const int32_t NT = cload(&hdr->n_tiles);
   const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
   const int32_t* nlen = reinterpret_cast<const int32_t*>(a.ws + a.off_nlen);
   const int unit = blockIdx.x;
-  const int32_t x0 = tile_begin(unit, NT, a.units);
-  const int32_t x1 = tile_begin(unit + 1, NT, a.units);
+  // The unit's descriptor from the plan (one scalar fetch): tile range, the
+  // sequence owning its first tile and that sequence's tile range and length.
+  const int32_t* ud = reinterpret_cast<const int32_t*>(a.ws + a.off_udesc) + unit * kUnitDescInts;
+  const int32_t x0 = cload(ud + 0);
+  const int32_t x1 = cload(ud + 1);
   if (x0 >= x1) return;
-
-  // Sequence owning tile x0: the largest b with cum[b] <= x0.
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cload(cum + mid) <= x0) lo = mid; else hi = mid - 1;
-  }
+  const int lo = cload(ud + 2);
 
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
   uint32_t bad_page = 0;
@@ -185,7 +181,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(Decode
 
   // ---- load cursor: runs two tiles ahead of the compute cursor
   int pb = lo;
-  int32_t pb_start = cload(cum + pb), pb_end = cload(cum + pb + 1), pb_n = cload(nlen + pb);
+  int32_t pb_start = cload(ud + 3), pb_end = cload(ud + 4), pb_n = cload(ud + 5);
   bool use_tab = false;
   auto lookup = [&](int b, int32_t pidx) __attribute__((always_inline)) -> int32_t {
     int32_t phys = a.page_table ? cload(a.page_table + static_cast<int64_t>(b) * a.max_pages + pidx)

@@ -31,13 +31,16 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 constexpr uint32_t kWsMagic = 0x4d4c5241u;  // "MLRA"
 constexpr uint32_t kFlagBadPage = 1u;       // same value as MLRA_FLAG_BAD_PAGE
 constexpr int kMaxBatch = 4096;             // sequences per call (the plan keeps them in LDS)
+// Per-unit descriptor written by the plan: {first tile, end tile, sequence of
+// the first tile, that sequence's first tile, its end tile, its length, 0, 0}.
+constexpr int kUnitDescInts = 8;
 
 // Everything a decode kernel needs, passed by value.
 struct DecodeArgs {
   const void* pool;
   const int32_t* page_table;  // nullptr: identity layout
   char* ws;
-  int64_t off_cum, off_nlen, off_sunit, off_qext, off_pm, off_pl, off_po;
+  int64_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po;
   int32_t batch;
   int32_t n_heads;
   int32_t d_h;
