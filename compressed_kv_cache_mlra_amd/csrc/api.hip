@@ -227,6 +227,7 @@ int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_ta
   st = check_append(desc);
   if (st != MLRA_OK) return st;
   if (!pool || !positions || !x || !w_dkv || (desc->d_r > 0 && !kr_new)) return MLRA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(w_dkv) % 16 != 0) return MLRA_ERR_INVALID_ARG;  // 16-byte row loads
   AppendArgs a;
   memset(&a, 0, sizeof(a));
   a.pool = pool;

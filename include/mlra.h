@@ -102,8 +102,9 @@ size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len);
  *   c_new[b] = x[b] W^DKV, accumulated in fp32 and rounded once to dtype
  *   (round to nearest, ties to even), then the row [c_new[b] | kr_new[b]] is
  *   written to the pool slot of token positions[b] of sequence b.
- *   x: [batch][d_model]; w_dkv: [d_model][d_c]; kr_new: [batch][d_r] (already
- *   rotated); positions: int32 [batch] (device); c_out: [batch][d_c] or NULL.
+ *   x: [batch][d_model]; w_dkv: [d_model][d_c], 16-byte aligned (else
+ *   MLRA_ERR_INVALID_ARG); kr_new: [batch][d_r] (already rotated); positions:
+ *   int32 [batch] (device); c_out: [batch][d_c] or NULL.
  * A position outside [0, max_pages_per_seq * page_size) writes nothing. The
  * caller advances its sequence lengths itself. */
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,

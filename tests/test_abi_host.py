@@ -130,6 +130,8 @@ def test_combine_and_append_validation():
         mlra.ERR_INVALID_ARG
     assert L.mlra_append_latent(ctypes.byref(d2), FAKE, None, FAKE, FAKE, FAKE, None, None, None) == \
         mlra.ERR_INVALID_ARG  # k^R_new required when d_r > 0
+    assert L.mlra_append_latent(ctypes.byref(d2), FAKE, None, FAKE, FAKE, ctypes.c_void_p(0x1008), FAKE,
+                                None, None) == mlra.ERR_INVALID_ARG  # W^DKV not 16-byte aligned
 
 
 def test_read_flags_validation():

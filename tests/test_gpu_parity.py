@@ -107,11 +107,23 @@ def test_full_size_workload5_with_append():
     _say(f"workload 5 full: max err/rms {err:.2e}")
 
 
-def test_append_exact_and_canary():
+APPEND_SHAPES = [
+    dict(n_heads=8, d_h=32, d_c=128, n_blocks=2, d_r=32, dtype="bf16", d_model=256),
+    dict(n_heads=8, d_h=32, d_c=128, n_blocks=2, d_r=32, dtype="f32", d_model=256),
+    # x staged in LDS in several chunks, partial last chunk
+    dict(n_heads=8, d_h=32, d_c=512, n_blocks=2, d_r=64, dtype="bf16", d_model=5000),
+    # fp32 latent whose last 8-column group holds 4 columns
+    dict(n_heads=8, d_h=32, d_c=132, n_blocks=1, d_r=16, dtype="f32", d_model=4100),
+]
+
+
+@pytest.mark.parametrize("kw", APPEND_SHAPES)
+def test_append_exact_and_canary(kw):
     """Append writes exactly the target rows; every other pool byte is unchanged."""
-    _say("case: append exactness")
-    for dtype in ("bf16", "f32"):
-        s = synth.Shape(batch=5, n_heads=8, d_h=32, d_c=128, n_blocks=2, d_r=32, dtype=dtype, d_model=256)
+    _say(f"case: append exactness {kw}")
+    dtype = kw["dtype"]
+    if True:
+        s = synth.Shape(batch=5, **kw)
         inp = synth.make_inputs(s, ("list_append", [0, 63, 64, 127, 500]), 77)
         prob = _gpu.GpuProblem(inp)
         before = _gpu.from_dev_bits(prob.pool).copy()
@@ -124,7 +136,8 @@ def test_append_exact_and_canary():
             d = np.abs(c_gpu.astype(np.int32) - c_ref.astype(np.int32))
             assert d.max() <= 1
         else:
-            assert np.allclose(c_gpu, c_ref, rtol=1e-5, atol=1e-6)
+            err = np.abs(c_gpu.astype(np.float64) - c_ref) / np.maximum(np.abs(c_ref), _gpu.rms(c_ref))
+            assert err.max() <= 1e-5, err.max()
         changed = np.zeros(before.shape[:2], dtype=bool)
         for b in range(s.batch):
             pos = int(inp.positions[b])
