@@ -57,6 +57,9 @@ struct Cfg {
   static constexpr int TASKS = NBR * HT;
   static constexpr int NWAVES = TASKS * G;
   static constexpr int NTHREADS = NWAVES * 64;
+  // waves per SIMD when OCC workgroups share a compute unit (the second
+  // __launch_bounds__ argument, which bounds the registers per wave)
+  static constexpr int WAVES_PER_SIMD = OCC * NWAVES / 4 > 1 ? OCC * NWAVES / 4 : 1;
   static constexpr int TILE_BYTES = TT * ROWB;
   static constexpr int TILE_CHUNKS = TT * CPR;
   // Loader threads: the largest multiple of 64 not above NTHREADS that divides
@@ -139,7 +142,7 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NTHREADS, C::OCC) void attend_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::TILE_BYTES];
   __shared__ int32_t ptab[C::PT_CAP];      // physical page of (tile - x0, page in tile)
   __shared__ int32_t seq_end[C::SEQ_WIN];  // cum[lo + 1 + i]
@@ -501,8 +504,11 @@ constexpr Entry entry() {
 const Entry kVariants[] = {
     entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
     entry<512, 64, 1, 4, 1, 32, 1>(),   // MLA: one 512 latent, 64 heads
-    entry<128, 64, 1, 1, 4, 128, 1>(),  // one MLRA-4 block (a TP rank's share), <= 16 heads
-    entry<256, 64, 2, 2, 1, 32, 1>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
+    // one MLRA-4 block (a TP rank's share), <= 16 heads: one-wave workgroups,
+    // four per compute unit, each streaming its own 32-token tiles (measured
+    // 1.8x faster than four waves sharing 128-token tiles at one per unit)
+    entry<128, 64, 1, 1, 1, 32, 4>(),
+    entry<256, 64, 2, 2, 1, 32, 2>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
     entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
     entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
     entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
