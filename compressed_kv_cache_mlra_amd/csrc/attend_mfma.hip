@@ -94,6 +94,10 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// s_waitcnt immediate for vmcnt(0) alone on gfx9: vmcnt bits [3:0] and
+// [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -350,11 +354,26 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     // tile x-1: tile x+1 goes registers -> the other buffer, tile x+2 is
     // requested into the registers.
     lds_barrier();
-    if (x + 1 < x1) {
-      store_tile(ring, lds + ((t + 1) & 1) * C::TILE_BYTES, store_valid(x + 1));
+    if constexpr (C::OCC == 1) {
+      // One workgroup per compute unit: nothing else hides this workgroup's
+      // memory waits, so tile x+2 stays in flight while tile x is computed.
+      // The query of a new sequence is loaded and waited for first, so no
+      // path into the MFMAs has it outstanding.
+      if (x + 1 < x1) store_tile(ring, lds + ((t + 1) & 1) * C::TILE_BYTES, store_valid(x + 1));
+      if (need_q) {
+        load_q(cb);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
       if (x + 2 < x1) load_tile(x + 2, ring);
+    } else {
+      // Several workgroups per compute unit: each waits for its loads before
+      // computing and the others fill the wait.
+      if (x + 1 < x1) {
+        store_tile(ring, lds + ((t + 1) & 1) * C::TILE_BYTES, store_valid(x + 1));
+        if (x + 2 < x1) load_tile(x + 2, ring);
+      }
+      if (need_q) load_q(cb);  // a new sequence starts inside this unit
     }
-    if (need_q) load_q(cb);  // a new sequence starts inside this unit
 
 #pragma unroll
     for (int si = 0; si < C::SUBW; ++si) {
