@@ -18,7 +18,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 METHODS = {"MHA": 0, "MQA": 1, "GQA": 2, "MLA": 3, "MFA": 4, "TPA": 5, "MLRA": 6}
 
 
@@ -29,6 +29,7 @@ class OracleShape(ctypes.Structure):
         ("d_r", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("d_model", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double), ("out_scale", ctypes.c_double),
+        ("cache_scale", ctypes.c_double),
     ]
 
 
@@ -65,6 +66,10 @@ def lib():
         L.oracle_row_index.restype = ctypes.c_int64
         L.oracle_round_bf16.argtypes = [ctypes.c_double]
         L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_cache_elems_per_token.argtypes = [ctypes.c_int32] * 7
         L.oracle_cache_elems_per_token.restype = ctypes.c_double
         L.oracle_cache_elems_per_device.argtypes = [ctypes.c_int32] * 9
@@ -83,9 +88,10 @@ def shape_of(inp, softmax_scale: Optional[float] = None, out_scale: Optional[flo
         batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
         blocks_per_head=s.blocks_per_head, d_r=s.d_r, page_size=s.page_size,
         max_pages_per_seq=inp.max_pages_per_seq, d_model=s.d_model,
-        dtype=BF16 if s.dtype == "bf16" else F32,
+        dtype={"bf16": BF16, "f32": F32, "fp8": FP8}[s.dtype],
         softmax_scale=s.softmax_scale if softmax_scale is None else softmax_scale,
-        out_scale=s.out_scale if out_scale is None else out_scale)
+        out_scale=s.out_scale if out_scale is None else out_scale,
+        cache_scale=getattr(s, "cache_scale", 0.0))
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -144,7 +150,8 @@ def append(inp, pool: np.ndarray, c_out: bool = True):
     """Applies the latent append to `pool` in place; returns c_new [B][d_c]."""
     s = inp.shape
     shp = shape_of(inp)
-    c = np.zeros((s.batch, s.d_c), dtype=pool.dtype) if c_out else None
+    c_dtype = np.float32 if s.dtype == "fp8" else pool.dtype  # fp8: the latent before encoding
+    c = np.zeros((s.batch, s.d_c), dtype=c_dtype) if c_out else None
     lib().oracle_append(ctypes.byref(shp), _ptr(pool), _iptr(inp.page_table), _iptr(inp.positions),
                         _ptr(inp.x), _ptr(inp.w_dkv), _ptr(inp.kr_new), _ptr(c))
     return c
@@ -163,6 +170,24 @@ def row_index(inp, b: int, t: int, page_table=None) -> int:
 
 def round_bf16(v: float) -> int:
     return int(lib().oracle_round_bf16(float(v)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(x)))
+
+
+def e4m3_encode_array(a: np.ndarray) -> np.ndarray:
+    """Encodes every fp32 value of `a` (a loop over the scalar oracle encoder)."""
+    flat = np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint8)
+    enc = lib().oracle_e4m3_encode
+    for i, v in enumerate(flat.tolist()):
+        out[i] = enc(v)
+    return out.reshape(np.shape(a))
 
 
 def cache_elems_per_token(method: str, h=0, d_h=0, g=0, beta_kv=0, d_c=0, d_r=0) -> float:

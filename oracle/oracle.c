@@ -74,6 +74,57 @@ uint16_t oracle_round_bf16(double v) {
   return (uint16_t)((u >> 16) | sign);
 }
 
+/* OCP FP8 E4M3FN (see oracle.h). A normal code e.m (e >= 1) is
+ * (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); a subnormal (e = 0) is m 2^-9. */
+double oracle_e4m3_decode(uint8_t code) {
+  const int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return sgn ? -v : v;
+}
+
+/* Codes in the binade [2^E, 2^(E+1)) (E >= -6) are spaced 2^(E-3); below 2^-6
+ * the subnormal spacing 2^-9 continues. With E' = max(E, -6) the nearest
+ * multiple n 2^(E'-3) of |x| (n in 0..16) has code (E' + 6) 8 + n, which also
+ * covers n = 16 (the next binade) and the subnormal range (E' = -6). */
+uint8_t oracle_e4m3_encode(float x) {
+  if (x != x) return 0x7F;
+  const uint8_t sgn = signbit(x) ? 0x80 : 0;
+  const double a = fabs((double)x);
+  if (a >= 448.0) return sgn | 0x7E;
+  int e2;
+  frexp(a, &e2); /* a = f 2^e2 with f in [0.5, 1): floor(log2 a) = e2 - 1 */
+  int E = a == 0.0 ? -6 : e2 - 1;
+  if (E < -6) E = -6;
+  const double n = rint(ldexp(a, 3 - E)); /* exact scaling, ties to even */
+  return sgn | (uint8_t)((E + 6) * 8 + (int)n);
+}
+
+/* Latent value `col` and RoPE value `r` of pool row `row_idx`. */
+static double pool_latent(const oracle_shape* s, const void* pool, int64_t row_idx, int32_t col) {
+  if (s->dtype == ORACLE_FP8_E4M3) {
+    const int64_t rb = s->d_c + 2 * (int64_t)s->d_r;
+    const double cs = s->cache_scale > 0 ? s->cache_scale : 1.0;
+    return oracle_e4m3_decode(((const uint8_t*)pool)[row_idx * rb + col]) * cs;
+  }
+  return elem(s->dtype, pool, row_idx * (s->d_c + s->d_r) + col);
+}
+
+static double pool_rope(const oracle_shape* s, const void* pool, int64_t row_idx, int32_t r) {
+  if (s->dtype == ORACLE_FP8_E4M3) {
+    const int64_t rb = s->d_c + 2 * (int64_t)s->d_r;
+    uint16_t v;
+    memcpy(&v, (const uint8_t*)pool + row_idx * rb + s->d_c + 2 * (int64_t)r, 2);
+    return elem(ORACLE_BF16, &v, 0);
+  }
+  return elem(s->dtype, pool, row_idx * (s->d_c + s->d_r) + s->d_c + r);
+}
+
+/* Encoding of the non-cache arrays (queries, weights, x, k^R_new). */
+static int32_t arrays_dtype(const oracle_shape* s) {
+  return s->dtype == ORACLE_FP8_E4M3 ? ORACLE_BF16 : s->dtype;
+}
+
 static void store_elem(int32_t dtype, void* base, int64_t idx, double v) {
   if (dtype == ORACLE_BF16)
     ((uint16_t*)base)[idx] = oracle_round_bf16(v);
@@ -115,9 +166,8 @@ void oracle_decode_unabsorbed(const oracle_shape* s, const void* pool, const int
                               double* lse) {
   const int32_t H = s->n_heads, DH = s->d_h, DR = s->d_r, K = s->blocks_per_head;
   const int32_t W = s->d_c / s->n_blocks;
-  const int32_t ROW = s->d_c + s->d_r;
   const double sigma = scale_of(s), alpha = out_scale_of(s);
-  const int32_t dt = s->dtype;
+  const int32_t dt = arrays_dtype(s);
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int32_t p = 0; p < npairs; ++p) {
@@ -148,14 +198,14 @@ void oracle_decode_unabsorbed(const oracle_shape* s, const void* pool, const int
       /* pass 1: reconstruct the key of every token and score it */
       double m = -INFINITY;
       for (int32_t t = 0; t < n; ++t) {
-        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
-        for (int32_t cc = 0; cc < W; ++cc) c[cc] = elem(dt, pool, row + (int64_t)j * W + cc);
+        const int64_t row = oracle_row_index(s, page_table, b, t);
+        for (int32_t cc = 0; cc < W; ++cc) c[cc] = pool_latent(s, pool, row, j * W + cc);
         for (int32_t d = 0; d < DH; ++d) kvec[d] = 0.0;
         for (int32_t cc = 0; cc < W; ++cc) /* K_t = W^UK_{i,j}^T c_{t,j} */
           for (int32_t d = 0; d < DH; ++d) kvec[d] += wk[(int64_t)cc * DH + d] * c[cc];
         double content = 0.0, rope = 0.0;
         for (int32_t d = 0; d < DH; ++d) content += q[d] * kvec[d];
-        for (int32_t r = 0; r < DR; ++r) rope += q[DH + r] * elem(dt, pool, row + s->d_c + r);
+        for (int32_t r = 0; r < DR; ++r) rope += q[DH + r] * pool_rope(s, pool, row, r);
         score[t] = sigma * (content + rope);
         if (score[t] > m) m = score[t];
       }
@@ -164,8 +214,8 @@ void oracle_decode_unabsorbed(const oracle_shape* s, const void* pool, const int
       for (int32_t t = 0; t < n; ++t) denom += exp(score[t] - m);
       for (int32_t t = 0; t < n; ++t) {
         const double pt = exp(score[t] - m) / denom;
-        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
-        for (int32_t cc = 0; cc < W; ++cc) c[cc] = elem(dt, pool, row + (int64_t)j * W + cc);
+        const int64_t row = oracle_row_index(s, page_table, b, t);
+        for (int32_t cc = 0; cc < W; ++cc) c[cc] = pool_latent(s, pool, row, j * W + cc);
         for (int32_t d = 0; d < DH; ++d) kvec[d] = 0.0; /* reused as V_t */
         for (int32_t cc = 0; cc < W; ++cc)
           for (int32_t d = 0; d < DH; ++d) kvec[d] += wv[(int64_t)cc * DH + d] * c[cc];
@@ -186,9 +236,8 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
                             double* lse) {
   const int32_t H = s->n_heads, DH = s->d_h, DR = s->d_r, K = s->blocks_per_head;
   const int32_t W = s->d_c / s->n_blocks;
-  const int32_t ROW = s->d_c + s->d_r;
   const double sigma = scale_of(s), alpha = out_scale_of(s);
-  const int32_t dt = s->dtype;
+  const int32_t dt = arrays_dtype(s);
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int32_t p = 0; p < npairs; ++p) {
@@ -214,11 +263,11 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
       }
       double m = -INFINITY;
       for (int32_t t = 0; t < n; ++t) {
-        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
+        const int64_t row = oracle_row_index(s, page_table, b, t);
         double v = 0.0;
-        for (int32_t cc = 0; cc < W; ++cc) v += qt[cc] * elem(dt, pool, row + (int64_t)j * W + cc);
+        for (int32_t cc = 0; cc < W; ++cc) v += qt[cc] * pool_latent(s, pool, row, j * W + cc);
         for (int32_t r = 0; r < DR; ++r)
-          v += elem(dt, q_r, ((int64_t)b * H + i) * DR + r) * elem(dt, pool, row + s->d_c + r);
+          v += elem(dt, q_r, ((int64_t)b * H + i) * DR + r) * pool_rope(s, pool, row, r);
         score[t] = sigma * v;
         if (score[t] > m) m = score[t];
       }
@@ -227,8 +276,8 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
       for (int32_t cc = 0; cc < W; ++cc) acc[cc] = 0.0;
       for (int32_t t = 0; t < n; ++t) {
         const double pt = exp(score[t] - m) / denom;
-        const int64_t row = oracle_row_index(s, page_table, b, t) * ROW;
-        for (int32_t cc = 0; cc < W; ++cc) acc[cc] += pt * elem(dt, pool, row + (int64_t)j * W + cc);
+        const int64_t row = oracle_row_index(s, page_table, b, t);
+        for (int32_t cc = 0; cc < W; ++cc) acc[cc] += pt * pool_latent(s, pool, row, j * W + cc);
       }
       for (int32_t d = 0; d < DH; ++d) {
         double v = 0.0;
@@ -247,6 +296,23 @@ void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
                    const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
                    void* c_out) {
   const int32_t DC = s->d_c, DR = s->d_r, DM = s->d_model, ROW = s->d_c + s->d_r;
+  if (s->dtype == ORACLE_FP8_E4M3) {
+    const int64_t rb = DC + 2 * (int64_t)DR;
+    const float inv = 1.0f / (float)(s->cache_scale > 0 ? s->cache_scale : 1.0);
+    for (int32_t b = 0; b < s->batch; ++b) {
+      uint8_t* row = (uint8_t*)pool + oracle_row_index(s, page_table, b, positions[b]) * rb;
+      for (int32_t cc = 0; cc < DC; ++cc) {
+        double v = 0.0;
+        for (int32_t m = 0; m < DM; ++m)
+          v += elem(ORACLE_BF16, x, (int64_t)b * DM + m) * elem(ORACLE_BF16, w_dkv, (int64_t)m * DC + cc);
+        const float cf = (float)v;
+        row[cc] = oracle_e4m3_encode(cf * inv);
+        if (c_out) ((float*)c_out)[(int64_t)b * DC + cc] = cf;
+      }
+      memcpy(row + DC, (const uint16_t*)kr_new + (int64_t)b * DR, 2 * (size_t)DR);
+    }
+    return;
+  }
   const int32_t dt = s->dtype;
   for (int32_t b = 0; b < s->batch; ++b) {
     const int64_t row = oracle_row_index(s, page_table, b, positions[b]) * ROW;

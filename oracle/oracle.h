@@ -20,8 +20,12 @@ extern "C" {
 #endif
 
 /* Element encodings the oracle reads: IEEE fp32 values, or bf16 bit patterns
- * (upper half of an fp32), which widen to double exactly. */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+ * (upper half of an fp32), which widen to double exactly. ORACLE_FP8_E4M3
+ * selects a quantised cache (the FP8 latent quantisation the lesty.tech MLA
+ * explainer mentions in section 5): cache rows hold the latent as OCP FP8
+ * E4M3FN codes followed by the RoPE key in bf16, every latent value being
+ * (decoded code) x cache_scale; all other arrays are then bf16. */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
 
 /* Problem shape, in the notation of the MLRA paper page (Table 6 notation):
  * h query heads of width d_h; a latent of width d_c cut into n_blocks blocks of
@@ -41,6 +45,7 @@ typedef struct {
   int32_t dtype;           /* ORACLE_F32 or ORACLE_BF16, for every input array */
   double softmax_scale;    /* <= 0 selects 1 / sqrt(d_h + d_r) */
   double out_scale;        /* <= 0 selects 1 / sqrt(blocks_per_head) */
+  double cache_scale;      /* FP8 caches: scale of every latent code (<= 0 selects 1) */
 } oracle_shape;
 
 /* Block attended by head `head` in its `jj`-th slot (0 <= jj < k). */
@@ -54,7 +59,8 @@ int64_t oracle_row_index(const oracle_shape* s, const int32_t* page_table, int32
  * K = W^UK c and V = W^UV c per cached token, scores with the content and the
  * decoupled RoPE terms, applies a two-pass softmax per attended block and sums
  * the per-block outputs times out_scale.
- *   pool:       [pages][page_size][d_c + d_r] elements
+ *   pool:       [pages][page_size][d_c + d_r] elements; for FP8 caches
+ *               [pages][page_size] rows of d_c code bytes then d_r bf16
  *   q_c:        [batch][h][d_h], q_r: [batch][h][d_r]
  *   w_uk, w_uv: [h][k][d_c / n_blocks][d_h]
  *   out:        [npairs][d_h] doubles, lse: [npairs][k] doubles (natural log) */
@@ -76,6 +82,8 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
 /* Latent append: c = x W^DKV accumulated in double and rounded once to the
  * storage type (round to nearest, ties to even), written with kr_new into the
  * row of token positions[b]; c_out (nullable) receives the rounded latent.
+ * FP8 caches: c is rounded to fp32, multiplied in fp32 by the fp32 reciprocal
+ * of cache_scale and encoded; c_out then receives the fp32 c (before encoding).
  *   x: [batch][d_model], w_dkv: [d_model][d_c], kr_new: [batch][d_r] */
 void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
                    const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
@@ -83,6 +91,14 @@ void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
 
 /* Rounds a double to a bf16 bit pattern, nearest with ties to even. */
 uint16_t oracle_round_bf16(double v);
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, subnormals,
+ * no infinities, S.1111.111 is NaN, largest finite magnitude 448.
+ * decode: the exact value of a code (NaN for the NaN codes).
+ * encode: nearest code to an fp32 value, ties to even, magnitudes of 448 and
+ * above saturate to 448, NaN gives 0x7F. */
+double oracle_e4m3_decode(uint8_t code);
+uint8_t oracle_e4m3_encode(float x);
 
 /* KV-cache elements loaded per token per device (Table 1 of the MLRA paper
  * page), for the methods listed there plus MLRA's block split.

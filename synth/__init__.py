@@ -17,6 +17,13 @@ Rows of the pool that hold no token (the tail of each sequence's last page, a
 spare page per sequence for the append target, and one guard page that unused
 page-table entries point at) are filled with a NaN canary so that a kernel that
 reads outside the sequence shows up as NaN in its outputs.
+
+FP8 caches (dtype "fp8"): a row is d_c bytes of OCP E4M3FN codes followed by the
+RoPE key as d_r bf16 values. Step 3 then draws each code's fields directly as
+integers (sign uniform in {0, 1}, exponent field uniform in 4..9, mantissa field
+uniform in 0..7: magnitudes between 1/8 and 7.5, no zeros or NaN) and the RoPE
+key N(0, 1) in bf16; every other array is bf16. The NaN canary is code 0x7F and
+the bf16 NaN.
 """
 from __future__ import annotations
 
@@ -38,13 +45,14 @@ class Shape:
     d_c: int
     n_blocks: int
     d_r: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (E4M3FN latent codes, bf16 everything else)
     page_size: int = 64
     blocks_per_head: int = 1
     d_model: int = 0
     paged: bool = True  # False: identity page layout (page table omitted)
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_h + d_r)
     out_scale: float = 0.0  # 0 -> 1/sqrt(blocks_per_head)
+    cache_scale: float = 0.0  # fp8: latent value = decoded code x cache_scale (0 -> 1)
 
     @property
     def w(self) -> int:
@@ -53,6 +61,17 @@ class Shape:
     @property
     def row(self) -> int:
         return self.d_c + self.d_r
+
+    @property
+    def row_bytes(self) -> int:
+        if self.dtype == "fp8":
+            return self.d_c + 2 * self.d_r
+        return self.row * (2 if self.dtype == "bf16" else 4)
+
+    @property
+    def arrays_dtype(self) -> str:
+        """Encoding of queries, weights and append inputs."""
+        return "bf16" if self.dtype == "fp8" else self.dtype
 
     @property
     def heads_per_block(self) -> int:
@@ -78,6 +97,11 @@ WORKLOADS = {
             shape=Shape(batch=16, n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="bf16",
                         d_model=4096),
             lengths=("uniform_append", 1024, 131072)),
+    # the FP8 latent cache of the next-step list: workload 2's shape with E4M3FN codes
+    6: dict(name="MLRA-4 fp8-e4m3 cache (scale 0.5), B=32 h=64 d_h=128 d_c=512(4x128) d_r=64 ctx=8192 paged",
+            shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
+                        cache_scale=0.5),
+            lengths=("fixed", 8192)),
 }
 
 
@@ -112,7 +136,7 @@ class Inputs:
     seq_lens: np.ndarray  # int32 [B], lengths the decode attends
     page_table: Optional[np.ndarray]  # int32 [B][max_pages] or None (identity layout)
     max_pages_per_seq: int
-    pool: np.ndarray  # [pages][page_size][row], uint16 (bf16 bits) or float32
+    pool: np.ndarray  # [pages][page_size][row], uint16 (bf16 bits) or float32; fp8: uint8 [..][row_bytes]
     q_c: np.ndarray
     q_r: np.ndarray
     w_uk: np.ndarray
@@ -126,6 +150,26 @@ class Inputs:
     @property
     def max_seq_len(self) -> int:
         return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+
+def _fp8_pool(rng: np.random.Generator, pages_rows, d_c: int, d_r: int) -> np.ndarray:
+    """FP8 cache rows: E4M3FN code fields drawn as integers, then the bf16 RoPE key."""
+    size = tuple(pages_rows) + (d_c,)
+    sign = rng.integers(0, 2, size=size, dtype=np.uint8)
+    expo = rng.integers(4, 10, size=size, dtype=np.uint8)
+    mant = rng.integers(0, 8, size=size, dtype=np.uint8)
+    rope = _normal(rng, tuple(pages_rows) + (d_r,), 1.0, "bf16")
+    pool = np.empty(tuple(pages_rows) + (d_c + 2 * d_r,), dtype=np.uint8)
+    pool[..., :d_c] = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
+    pool[..., d_c:] = rope.view(np.uint8).reshape(tuple(pages_rows) + (2 * d_r,))
+    return pool
+
+
+def _FP8_NAN_ROW(d_c: int, d_r: int) -> np.ndarray:
+    row = np.empty(d_c + 2 * d_r, dtype=np.uint8)
+    row[:d_c] = 0x7F
+    row[d_c:] = np.full(d_r, BF16_NAN, dtype=np.uint16).view(np.uint8)
+    return row
 
 
 def _normal(rng: np.random.Generator, shape, scale: float, dtype: str) -> np.ndarray:
@@ -185,9 +229,13 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
     row = shape.row
     pools = []
     for _ in range(pool_copies):
-        pool = _normal(rng, (n_pages, P, row), 1.0, shape.dtype)
-        if canary:
+        if shape.dtype == "fp8":
+            pool = _fp8_pool(rng, (n_pages, P), shape.d_c, shape.d_r)
+            nanv = _FP8_NAN_ROW(shape.d_c, shape.d_r)
+        else:
+            pool = _normal(rng, (n_pages, P, row), 1.0, shape.dtype)
             nanv = BF16_NAN if shape.dtype == "bf16" else F32_NAN
+        if canary:
             for b in range(B):
                 valid = int(n[b]) - (1 if append else 0)  # rows written so far
                 for pi, page in enumerate(phys_of[b]):
@@ -202,19 +250,20 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
                         pool[b * max_pages + pi] = nanv
         pools.append(pool)
     H, DH, DR, K, W = shape.n_heads, shape.d_h, shape.d_r, shape.blocks_per_head, shape.w
-    q_c = _normal(rng, (B, H, DH), 1.0, shape.dtype)
-    q_r = _normal(rng, (B, H, DR), 1.0, shape.dtype)
-    w_uk = _normal(rng, (H, K, W, DH), 1.0 / math.sqrt(W), shape.dtype)
-    w_uv = _normal(rng, (H, K, W, DH), 1.0 / math.sqrt(W), shape.dtype)
+    adt = shape.arrays_dtype
+    q_c = _normal(rng, (B, H, DH), 1.0, adt)
+    q_r = _normal(rng, (B, H, DR), 1.0, adt)
+    w_uk = _normal(rng, (H, K, W, DH), 1.0 / math.sqrt(W), adt)
+    w_uv = _normal(rng, (H, K, W, DH), 1.0 / math.sqrt(W), adt)
     inp = Inputs(shape=shape, seq_lens=n.astype(np.int32), page_table=page_table,
                  max_pages_per_seq=max_pages, pool=pools[0] if pool_copies == 1 else pools,
                  q_c=q_c, q_r=q_r, w_uk=w_uk, w_uv=w_uv)
     if append:
         DM = shape.d_model
         inp.positions = pre.astype(np.int32)
-        inp.x = _normal(rng, (B, DM), 1.0, shape.dtype)
-        inp.w_dkv = _normal(rng, (DM, shape.d_c), 1.0 / math.sqrt(DM), shape.dtype)
-        inp.kr_new = _normal(rng, (B, DR), 1.0, shape.dtype)
+        inp.x = _normal(rng, (B, DM), 1.0, adt)
+        inp.w_dkv = _normal(rng, (DM, shape.d_c), 1.0 / math.sqrt(DM), adt)
+        inp.kr_new = _normal(rng, (B, DR), 1.0, adt)
     return inp
 
 

@@ -470,3 +470,111 @@ def test_synth_deterministic():
         assert np.array_equal(getattr(a, k).view(np.uint8), getattr(b, k).view(np.uint8)), k
     assert np.all(a.seq_lens == a.positions + 1)
     assert a.seq_lens.min() >= 1025 and a.seq_lens.max() <= 4097
+
+
+# ---------------------------------------------------------------- FP8 cache
+# The lesty.tech MLA explainer (section 5) notes that the cached latent can be
+# quantised with FP8 frameworks; the encoding here is OCP FP8 E4M3FN with one
+# scale per cache (the readings are listed in the design notes).
+
+E4M3_KNOWN = {  # code -> value, from the OCP 8-bit floating point specification's E4M3 table
+    0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 0.875 * 2.0 ** -6, 0x08: 2.0 ** -6,
+    0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0,
+}
+
+
+def test_e4m3_decode_known_values_and_library():
+    for code, v in E4M3_KNOWN.items():
+        assert oracle.e4m3_decode(code) == v and math.copysign(1, oracle.e4m3_decode(code)) == math.copysign(1, v)
+    assert math.isnan(oracle.e4m3_decode(0x7F)) and math.isnan(oracle.e4m3_decode(0xFF))
+    torch = pytest.importorskip("torch")
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mine = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    same = (mine == lib) | (np.isnan(mine) & np.isnan(lib))
+    assert same.all(), np.nonzero(~same)
+
+
+def test_e4m3_encode_roundtrip_ties_and_saturation():
+    # every finite code is a fixed point of encode(decode(.))
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c, hex(c)
+    # midpoints between neighbouring positive codes go to the even code
+    for c in range(0x00, 0x7E):
+        lo, hi = oracle.e4m3_decode(c), oracle.e4m3_decode(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        if float(mid) != (lo + hi) / 2:
+            continue  # not exactly representable in fp32
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(float(mid)) == want, hex(c)
+    # saturation (the reading chosen for values past the largest finite code) and NaN
+    for v, code in ((448.0, 0x7E), (463.9, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (-1e30, 0xFE)):
+        assert oracle.e4m3_encode(v) == code, v
+    assert oracle.e4m3_encode(float("nan")) == 0x7F
+
+
+def test_e4m3_encode_matches_library_in_range():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 0.1, 1.0, 30.0, 150.0)]).astype(np.float32)
+    x = x[np.abs(x) < 464.0]  # the library rounds past the largest code to NaN; the oracle saturates
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode_array(x), lib)
+
+
+def _fp8_and_bf16_twin(seed, lengths, cache_scale, **kw):
+    """An FP8 problem and a bf16 problem whose latents hold exactly the FP8
+    problem's dequantised values (E4M3 values times a power of two are bf16)."""
+    s8 = synth.Shape(dtype="fp8", cache_scale=cache_scale, **kw)
+    inp8 = synth.make_inputs(s8, lengths, seed)
+    codes = inp8.pool[..., :s8.d_c]
+    table = np.array([oracle.e4m3_decode(c) for c in range(256)]) * (cache_scale or 1.0)
+    lat = synth.f32_to_bf16_bits(table[codes].astype(np.float32))
+    rope = np.ascontiguousarray(inp8.pool[..., s8.d_c:]).view(np.uint16)
+    s16 = synth.Shape(dtype="bf16", **kw)
+    inp16 = synth.make_inputs(s16, lengths, seed)
+    inp16.pool = np.ascontiguousarray(np.concatenate([lat, rope], axis=-1))
+    for f in ("page_table", "seq_lens", "q_c", "q_r", "w_uk", "w_uv", "max_pages_per_seq"):
+        setattr(inp16, f, getattr(inp8, f))
+    return inp8, inp16
+
+
+def test_fp8_cache_decodes_like_its_bf16_twin():
+    """An FP8 cache reads as (decoded code) x cache_scale for the latent and as
+    bf16 for the RoPE key: the oracle's result equals the bf16 path's (itself
+    pinned to textbook attention) on the dequantised twin, canaries included."""
+    inp8, inp16 = _fp8_and_bf16_twin(21, ("list", [150, 1, 70]), 0.5, batch=3, n_heads=8, d_h=16,
+                                     d_c=64, n_blocks=4, d_r=16)
+    o8, l8 = oracle.decode_unabsorbed(inp8)
+    o16, l16 = oracle.decode_unabsorbed(inp16)
+    assert np.all(np.isfinite(o8))
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+    a8, al8 = oracle.decode_absorbed(inp8)
+    assert np.abs(a8 - o8).max() <= 1e-12 * np.abs(o8).max()
+
+
+def test_fp8_append_encodes_the_fp32_latent():
+    """FP8 append: c = x W^DKV (numpy float64 matmul), rounded to fp32, times
+    the fp32 reciprocal of cache_scale, encoded by the library's E4M3 rounding;
+    c_out holds the fp32 latent; the RoPE key lands as bf16; nothing else moves."""
+    torch = pytest.importorskip("torch")
+    s = synth.Shape(batch=3, n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16, dtype="fp8",
+                    cache_scale=0.25, d_model=96)
+    inp = synth.make_inputs(s, ("list_append", [0, 63, 200]), 8)
+    pool = inp.pool.copy()
+    c = oracle.append(inp, pool)
+    x = _f(inp.x)
+    w = _f(inp.w_dkv)
+    c_ref = (x @ w).astype(np.float32)
+    # summation order may move the fp32 rounding of a sum by one unit in the last place
+    assert np.all(np.abs(c - c_ref) <= 2 * np.spacing(np.abs(c_ref)))
+    want = torch.from_numpy(c * np.float32(1.0 / 0.25)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    changed = np.zeros(pool.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // s.page_size], pos % s.page_size
+        changed[pg, off] = True
+        assert np.array_equal(pool[pg, off, :s.d_c], want[b])
+        assert np.array_equal(pool[pg, off, s.d_c:].view(np.uint16), inp.kr_new[b])
+    assert np.array_equal(pool[~changed], inp.pool[~changed])
