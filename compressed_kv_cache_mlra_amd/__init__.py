@@ -21,10 +21,10 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmlra.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class MlraError(RuntimeError):
@@ -41,17 +41,20 @@ class MlraDesc(ctypes.Structure):
         ("d_r", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32), ("d_model", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("out_scale", ctypes.c_float),
+        ("cache_scale", ctypes.c_float),
     ]
 
 
 def make_desc(batch, n_heads, d_h, d_c, n_blocks, d_r, max_pages_per_seq, num_pages, dtype,
-              page_size=64, blocks_per_head=1, d_model=0, softmax_scale=0.0, out_scale=0.0) -> MlraDesc:
+              page_size=64, blocks_per_head=1, d_model=0, softmax_scale=0.0, out_scale=0.0,
+              cache_scale=0.0) -> MlraDesc:
     if isinstance(dtype, str):
-        dtype = {"f32": F32, "bf16": BF16}[dtype]
+        dtype = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}[dtype]
     return MlraDesc(batch=batch, n_heads=n_heads, d_h=d_h, d_c=d_c, n_blocks=n_blocks,
                     blocks_per_head=blocks_per_head, d_r=d_r, page_size=page_size,
                     max_pages_per_seq=max_pages_per_seq, num_pages=num_pages, d_model=d_model,
-                    dtype=dtype, softmax_scale=softmax_scale, out_scale=out_scale)
+                    dtype=dtype, softmax_scale=softmax_scale, out_scale=out_scale,
+                    cache_scale=cache_scale)
 
 
 _lib = None
@@ -103,8 +106,9 @@ def _torch():
 
 
 def _elem_dtype(desc: MlraDesc):
+    """Element type of queries, weights and append inputs (bf16 for FP8 caches)."""
     torch = _torch()
-    return torch.bfloat16 if desc.dtype == BF16 else torch.float32
+    return torch.float32 if desc.dtype == F32 else torch.bfloat16
 
 
 def _ptr(t, desc: Optional[MlraDesc] = None, kind: str = "float", name: str = "tensor",
@@ -159,6 +163,14 @@ def _row(desc):
     return desc.d_c + desc.d_r
 
 
+def _pool_ptr(pool, desc):
+    """The cache pool: elements of desc.dtype, or bytes for FP8 caches."""
+    if desc.dtype == FP8_E4M3:
+        return _ptr(pool, kind="bytes", name="pool",
+                    numel=desc.num_pages * desc.page_size * (desc.d_c + 2 * desc.d_r) // pool.element_size())
+    return _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc))
+
+
 def _w(desc):
     return desc.d_c // desc.n_blocks
 
@@ -167,13 +179,14 @@ def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=Non
     B = desc.batch
     _check(lib().mlra_append_latent(
         ctypes.byref(desc),
-        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _pool_ptr(pool, desc),
         _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
         _ptr(positions, kind="int32", name="positions", numel=B),
         _ptr(x, desc, name="x", numel=B * desc.d_model),
         _ptr(w_dkv, desc, name="w_dkv", numel=desc.d_model * desc.d_c),
         _ptr(kr_new, desc, name="kr_new", numel=B * desc.d_r, nullable=desc.d_r == 0),
-        _ptr(c_out, desc, name="c_out", numel=B * desc.d_c, nullable=True),
+        (_ptr(c_out, kind="f32", name="c_out", numel=B * desc.d_c, nullable=True) if desc.dtype == FP8_E4M3
+         else _ptr(c_out, desc, name="c_out", numel=B * desc.d_c, nullable=True)),
         _stream(stream)), "append_latent")
 
 
@@ -192,7 +205,7 @@ def absorb_query(desc, seq_lens, q_c, q_r, w_uk, workspace, stream=None):
 def attend(desc, pool, page_table, workspace, stream=None):
     _check(lib().mlra_attend(
         ctypes.byref(desc),
-        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _pool_ptr(pool, desc),
         _ptr(page_table, kind="int32", name="page_table", numel=desc.batch * desc.max_pages_per_seq,
              nullable=True),
         _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
@@ -203,7 +216,7 @@ def decode(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, worksp
     B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
     _check(lib().mlra_decode(
         ctypes.byref(desc),
-        _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc)),
+        _pool_ptr(pool, desc),
         _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
         _ptr(seq_lens, kind="int32", name="seq_lens", numel=B), ctypes.c_int32(int(max_seq_len)),
         _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),

@@ -2,9 +2,11 @@
 //
 // Absorption (lesty.tech MLA explainer, section 5; ai360xpert concept page,
 // "Absorbing the up-projection"): the key up-projection folds into the query,
-//   q~[b][i][jj][c] = s * sum_d W^UK[i][jj][c][d] q^C[b][i][d],
+//   q~[b][i][jj][c] = s z * sum_d W^UK[i][jj][c][d] q^C[b][i][d],
 // and the RoPE part of the query is only scaled, q^R~ = s * q^R, with
-// s = softmax_scale * log2(e) so the attention kernels work with base-2 logits.
+// s = softmax_scale * log2(e) so the attention kernels work with base-2 logits
+// and z the FP8 cache scale (1 for other caches), so that scores against the
+// raw E4M3 codes are scores against the latent values they stand for.
 #include "common.h"
 #include "launch.h"
 
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
 #pragma unroll
     for (int bl = 0; bl < kAbsorbBatchGroup; ++bl)
       if (bl < nb)
-        qext[(static_cast<int64_t>(b0 + bl) * HK + hk) * QW + c] = store_cast<TQ>(acc[bl] * a.qscale);
+        qext[(static_cast<int64_t>(b0 + bl) * HK + hk) * QW + c] = store_cast<TQ>(acc[bl] * (a.qscale * a.lat_scale));
   }
   for (int e = tid; e < nb * a.d_r; e += kAbsorbThreads) {
     const int bl = e / a.d_r, r = e % a.d_r;
@@ -208,10 +210,12 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
     }
     if (b_ok) {
       // lane holds rows c = mt*16 + 4 g4 + i of sequence b: 4 consecutive outputs
-      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[0] * a.qscale)) |
-                          (static_cast<uint32_t>(f32_to_bf16(acc[1] * a.qscale)) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[2] * a.qscale)) |
-                          (static_cast<uint32_t>(f32_to_bf16(acc[3] * a.qscale)) << 16);
+      // the latent part carries the FP8 cache scale (1 otherwise)
+      const float qs = a.qscale * a.lat_scale;
+      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[0] * qs)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[1] * qs)) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[2] * qs)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[3] * qs)) << 16);
       uint2* dst = reinterpret_cast<uint2*>(qext + (static_cast<int64_t>(b) * HK + hk) * QW + mt * 16 + 4 * g4);
       *dst = make_uint2(lo, hi);
     }

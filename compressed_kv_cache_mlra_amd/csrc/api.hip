@@ -39,8 +39,10 @@ int make_plan(const mlra_desc* d, Plan* p) {
   int st = check_desc(d, &p->s);
   if (st != MLRA_OK) return st;
   const ShapeInfo& s = p->s;
-  p->variant = d->dtype == MLRA_BF16 ? find_mfma_variant(s.w, d->d_r, d->n_blocks, s.head_tiles)
-                                     : nullptr;
+  const bool fp8 = d->dtype == MLRA_FP8_E4M3;
+  p->variant = d->dtype != MLRA_F32 ? find_mfma_variant(s.w, d->d_r, d->n_blocks, s.head_tiles, fp8)
+                                    : nullptr;
+  if (fp8 && !p->variant) return MLRA_ERR_UNSUPPORTED;  // FP8 caches run on the MFMA variants only
   if (p->variant) {
     p->tile_tokens = p->variant->tile_tokens;
     p->groups = p->variant->groups;
@@ -72,6 +74,11 @@ int make_plan(const mlra_desc* d, Plan* p) {
   off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk * s.w);
   p->total = off;
   return MLRA_OK;
+}
+
+// FP8 caches: the value one code unit stands for (1 for other caches).
+float cache_scale_of(const mlra_desc* d) {
+  return d->dtype == MLRA_FP8_E4M3 && d->cache_scale > 0.f ? d->cache_scale : 1.0f;
 }
 
 DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, const int32_t* pt,
@@ -111,10 +118,14 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.qscale = sigma * 1.4426950408889634f;
   a.out_scale = d->out_scale > 0.f ? d->out_scale
                                    : 1.0f / sqrtf(static_cast<float>(d->blocks_per_head));
+  a.lat_scale = cache_scale_of(d);
   return a;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLRA_OK : MLRA_ERR_HIP; }
+
+// Element type of queries, weights and append inputs (bf16 for FP8 caches).
+int arrays_dtype(const mlra_desc* d) { return d->dtype == MLRA_FP8_E4M3 ? MLRA_BF16 : d->dtype; }
 
 }  // namespace
 }  // namespace mlra
@@ -123,7 +134,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 1; }
+int mlra_abi_version(void) { return 2; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -154,7 +165,7 @@ int mlra_absorb_query(const mlra_desc* desc, const int32_t* seq_lens, const void
   if (!seq_lens || !q_c || !w_uk || !workspace || (desc->d_r > 0 && !q_r)) return MLRA_ERR_INVALID_ARG;
   if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
   DecodeArgs a = decode_args(desc, p, nullptr, nullptr, workspace);
-  return hip_status(launch_absorb(a, desc->dtype, p.q_bf16, seq_lens, q_c, q_r, w_uk,
+  return hip_status(launch_absorb(a, arrays_dtype(desc), p.q_bf16, seq_lens, q_c, q_r, w_uk,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -215,7 +226,8 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   c.empty_slot = static_cast<int32_t>(p.slots - 1);
   c.out_scale = desc->out_scale > 0.f ? desc->out_scale
                                       : 1.0f / sqrtf(static_cast<float>(desc->blocks_per_head));
-  return hip_status(launch_combine(c, desc->dtype, static_cast<hipStream_t>(stream)));
+  c.out_scale *= cache_scale_of(desc);  // FP8 caches: the partials sum codes, not latent values
+  return hip_status(launch_combine(c, arrays_dtype(desc), static_cast<hipStream_t>(stream)));
 }
 
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,
@@ -241,10 +253,11 @@ int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_ta
   a.d_c = desc->d_c;
   a.d_r = desc->d_r;
   a.d_model = desc->d_model;
-  a.row = desc->d_c + desc->d_r;
+  a.row = desc->dtype == MLRA_FP8_E4M3 ? desc->d_c + 2 * desc->d_r : desc->d_c + desc->d_r;
   a.page_size = desc->page_size;
   a.max_pages = desc->max_pages_per_seq;
   a.num_pages = desc->num_pages;
+  a.cache_inv = 1.0f / cache_scale_of(desc);
   return hip_status(launch_append(a, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -2,6 +2,9 @@
 // projections"; the cache keeps the latent, not per-head keys and values),
 // accumulated in fp32, rounded once to the cache type, and written with the
 // already-rotated RoPE key as the row [c_new | k^R_new] of token positions[b].
+// FP8 caches (the latent quantisation the lesty.tech MLA explainer mentions
+// in section 5) store each latent value as the nearest OCP E4M3FN code of
+// c_new times the reciprocal of the cache scale.
 #include "common.h"
 #include "launch.h"
 
@@ -39,12 +42,30 @@ struct Row8<float> {
   __device__ __forceinline__ float get(int j) const { return __uint_as_float(j < 4 ? v0[j] : v1[j - 4]); }
 };
 
+// Nearest OCP E4M3FN code of x, ties to even; magnitudes of 448 and above
+// saturate to 448 and NaN gives 0x7F. Codes in the binade [2^E, 2^(E+1))
+// (E >= -6) are spaced 2^(E-3) and the subnormal spacing 2^-9 continues below
+// 2^-6, so with E' = max(E, -6) the nearest multiple n 2^(E'-3) of |x|
+// (n in 0..16) has code (E' + 6) 8 + n.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (x != x) return 0x7Fu;
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a >= 448.f) return sgn | 0x7Eu;
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // floor(log2 a); zero -> -127
+  if (e < -6) e = -6;
+  const float n = rintf(a * __uint_as_float(static_cast<uint32_t>(130 - e) << 23));  // a 2^(3-e), exact
+  return sgn | static_cast<uint32_t>((e + 6) * 8 + static_cast<int>(n));
+}
+
 // grid: n_chunks * batch, chunk fastest, so consecutive workgroups (which the
 // dispatcher spreads over the 8 XCDs) cover different column chunks and each
 // XCD's L2 keeps reusing one chunk of W^DKV across the batch.
 // Thread (col group g, k lane kl) accumulates columns [8 g, 8 g + 8) of the
 // chunk over rows k = kl (mod 64) of W^DKV; the 64 k lanes are summed in LDS.
-template <typename T>
+// T: element type of x, W^DKV and k^R_new; F8: the pool is an FP8 cache
+// (codes then the bf16 RoPE key per row; c_out is fp32).
+template <typename T, bool F8>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int n_chunks) {
   __shared__ float xs[kXChunk];
   __shared__ float red[kKLanes][kCols + 1];
@@ -101,19 +122,32 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int n_ch
   int32_t phys = a.page_table ? a.page_table[static_cast<int64_t>(b) * a.max_pages + pidx]
                               : b * a.max_pages + pidx;
   if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) return;  // uniform
-  T* row = static_cast<T*>(a.pool) +
-           (static_cast<int64_t>(phys) * a.page_size + (pos % a.page_size)) * a.row;
+  const int64_t row_index = static_cast<int64_t>(phys) * a.page_size + (pos % a.page_size);
   const int col = chunk * kCols + tid;
-  if (tid < kCols && col < a.d_c) {
-    float v = 0.f;
-    for (int s = 0; s < kKLanes; ++s) v += red[s][tid];
-    const T o = store_cast<T>(v);
-    row[col] = o;
-    if (a.c_out) static_cast<T*>(a.c_out)[static_cast<int64_t>(b) * a.d_c + col] = o;
-  }
-  if (chunk == 0) {
-    const T* kr = static_cast<const T*>(a.kr_new) + static_cast<int64_t>(b) * a.d_r;
-    for (int r = tid; r < a.d_r; r += kThreads) row[a.d_c + r] = kr[r];
+  const T* kr = static_cast<const T*>(a.kr_new) + static_cast<int64_t>(b) * a.d_r;
+  if constexpr (F8) {
+    uint8_t* row = static_cast<uint8_t*>(a.pool) + row_index * a.row;  // a.row: bytes
+    if (tid < kCols && col < a.d_c) {
+      float v = 0.f;
+      for (int s = 0; s < kKLanes; ++s) v += red[s][tid];
+      row[col] = static_cast<uint8_t>(e4m3_encode(v * a.cache_inv));
+      if (a.c_out) static_cast<float*>(a.c_out)[static_cast<int64_t>(b) * a.d_c + col] = v;
+    }
+    if (chunk == 0) {
+      T* rope = reinterpret_cast<T*>(row + a.d_c);
+      for (int r = tid; r < a.d_r; r += kThreads) rope[r] = kr[r];
+    }
+  } else {
+    T* row = static_cast<T*>(a.pool) + row_index * a.row;
+    if (tid < kCols && col < a.d_c) {
+      float v = 0.f;
+      for (int s = 0; s < kKLanes; ++s) v += red[s][tid];
+      const T o = store_cast<T>(v);
+      row[col] = o;
+      if (a.c_out) static_cast<T*>(a.c_out)[static_cast<int64_t>(b) * a.d_c + col] = o;
+    }
+    if (chunk == 0)
+      for (int r = tid; r < a.d_r; r += kThreads) row[a.d_c + r] = kr[r];
   }
 }
 
@@ -122,10 +156,12 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a, int n_ch
 hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t stream) {
   const int n_chunks = (a.d_c + kCols - 1) / kCols;
   const dim3 grid(n_chunks * a.batch);
-  if (dtype == 1)
-    append_kernel<uint16_t><<<grid, kThreads, 0, stream>>>(a, n_chunks);
+  if (dtype == 2)
+    append_kernel<uint16_t, true><<<grid, kThreads, 0, stream>>>(a, n_chunks);
+  else if (dtype == 1)
+    append_kernel<uint16_t, false><<<grid, kThreads, 0, stream>>>(a, n_chunks);
   else
-    append_kernel<float><<<grid, kThreads, 0, stream>>>(a, n_chunks);
+    append_kernel<float, false><<<grid, kThreads, 0, stream>>>(a, n_chunks);
   return hipGetLastError();
 }
 

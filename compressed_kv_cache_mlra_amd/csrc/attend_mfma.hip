@@ -42,7 +42,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_>
+template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -52,8 +52,12 @@ struct Cfg {
   static constexpr int TT = TT_;    // tokens per tile
   static constexpr int OCC = OCC_;  // workgroups resident per compute unit
   static constexpr int ROW = NBR * W + DR;
-  static constexpr int ROWB = ROW * 2;
-  static constexpr int CPR = ROW / 8;  // 16-byte chunks per row
+  static constexpr bool F8 = F8_;     // cache rows hold E4M3FN latent codes, then bf16 k^R
+  static constexpr int ROWB = ROW * 2;  // bytes of a row in LDS (bf16 throughout)
+  static constexpr int CPR = ROW / 8;   // 16-byte LDS chunks per row
+  static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROWB;  // bytes of a row in HBM
+  static constexpr int CPRG = ROWG / 16;                     // 16-byte HBM chunks per row
+  static constexpr int LATC = F8 ? NBR * W / 16 : 0;         // HBM chunks of latent codes per row
   static constexpr int TASKS = NBR * HT;
   static constexpr int NWAVES = TASKS * G;
   static constexpr int NTHREADS = NWAVES * 64;
@@ -61,7 +65,7 @@ struct Cfg {
   // __launch_bounds__ argument, which bounds the registers per wave)
   static constexpr int WAVES_PER_SIMD = OCC * NWAVES / 4 > 1 ? OCC * NWAVES / 4 : 1;
   static constexpr int TILE_BYTES = TT * ROWB;
-  static constexpr int TILE_CHUNKS = TT * CPR;
+  static constexpr int TILE_CHUNKS = TT * CPRG;  // HBM chunks of one tile
   // Loader threads: the largest multiple of 64 not above NTHREADS that divides
   // the tile's chunk count, so every loader moves the same number of chunks.
   static constexpr int loaders() {
@@ -219,12 +223,12 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     if (P >= C::TT) {
       // the whole tile sits in one page: one base, per-lane offsets
       const uint8_t* base = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(
-          pool + (static_cast<int64_t>(page_of(x, 0)) * P + (tok0 & (P - 1))) * C::ROWB)));
+          pool + (static_cast<int64_t>(page_of(x, 0)) * P + (tok0 & (P - 1))) * C::ROWG)));
 #pragma unroll
       for (int k = 0; k < C::NL; ++k) {
         const int p = k * C::NLT + tid;
-        const int r = p / C::CPR, lc = p % C::CPR;
-        ring[k] = gload16_stream(base + r * C::ROWB + 16 * lc);
+        const int r = p / C::CPRG, lc = p % C::CPRG;
+        ring[k] = gload16_stream(base + r * C::ROWG + 16 * lc);
       }
     } else {
       // tile spans npt pages (tok0 is page aligned): per-lane page select
@@ -234,12 +238,12 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 #pragma unroll
       for (int k = 0; k < C::NL; ++k) {
         const int p = k * C::NLT + tid;
-        const int r = p / C::CPR, lc = p % C::CPR;
+        const int r = p / C::CPRG, lc = p % C::CPRG;
         const int j = r >> a.log2_page;
         int32_t phys = ph[0];
 #pragma unroll
         for (int q = 1; q < C::MAXPG; ++q) phys = j == q ? ph[q] : phys;
-        ring[k] = gload16_stream(pool + (static_cast<int64_t>(phys) * P + (r & (P - 1))) * C::ROWB + 16 * lc);
+        ring[k] = gload16_stream(pool + (static_cast<int64_t>(phys) * P + (r & (P - 1))) * C::ROWG + 16 * lc);
       }
     }
   };
@@ -249,10 +253,29 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 #pragma unroll
     for (int k = 0; k < C::NL; ++k) {
       const int p = k * C::NLT + tid;
-      const int r = p / C::CPR, lc = p % C::CPR;
+      const int r = p / C::CPRG, lc = p % C::CPRG;
       u32x4_t v = ring[k];
       if (r >= valid) v = u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (lc ^ (r & 7))) = v;
+      if constexpr (C::F8) {
+        if (lc < C::LATC) {
+          // 16 latent codes -> 16 bf16 values (exact: E4M3 values are bf16 values)
+          u32x4_t lo, hi;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            lo[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, false));
+            lo[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, true));
+            hi[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + h], 1.0f, false));
+            hi[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + h], 1.0f, true));
+          }
+          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * ((2 * lc) ^ (r & 7))) = lo;
+          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * ((2 * lc + 1) ^ (r & 7))) = hi;
+        } else {
+          const int chunk = C::NBR * C::W / 8 + (lc - C::LATC);  // the bf16 RoPE key, copied
+          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (chunk ^ (r & 7))) = v;
+        }
+      } else {
+        *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (lc ^ (r & 7))) = v;
+      }
     }
   };
 
@@ -513,10 +536,11 @@ struct Entry {
   hipError_t (*fn)(const DecodeArgs&, hipStream_t);
 };
 
-template <int W, int DR, int NBR, int HT, int G, int TT, int OCC>
+template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC>;
-  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, C::NTHREADS, 2 * C::TILE_BYTES}, &run_variant<C>};
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8>;
+  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? 1 : 0, C::NTHREADS, 2 * C::TILE_BYTES},
+               &run_variant<C>};
 }
 
 // Shapes with a tuned MFMA kernel. Key: (w, d_r, blocks per row, 16-head tiles per block).
@@ -531,13 +555,19 @@ const Entry kVariants[] = {
     entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
     entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
     entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
+    // FP8 (E4M3FN) caches of the same shapes and tunings
+    entry<128, 64, 4, 1, 1, 32, 2, true>(),
+    entry<512, 64, 1, 4, 1, 32, 1, true>(),
+    entry<128, 64, 1, 1, 1, 32, 4, true>(),
+    entry<256, 64, 2, 2, 1, 32, 2, true>(),
 };
 
 }  // namespace
 
-const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles) {
+const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles, bool fp8) {
   for (const Entry& e : kVariants)
-    if (e.v.w == w && e.v.d_r == d_r && e.v.n_blocks == n_blocks && e.v.head_tiles == head_tiles)
+    if (e.v.w == w && e.v.d_r == d_r && e.v.n_blocks == n_blocks && e.v.head_tiles == head_tiles &&
+        e.v.fp8 == (fp8 ? 1 : 0))
       return &e.v;
   return nullptr;
 }

@@ -60,6 +60,7 @@ struct DecodeArgs {
   int32_t empty_slot;  // partial slot kept empty (m = -inf, l = 0, o~ = 0) for the combine
   float qscale;       // softmax_scale * log2(e)
   float out_scale;
+  float lat_scale;    // FP8 caches: cache_scale (folded into the latent part of q~); else 1
 };
 
 struct AppendArgs {
@@ -70,7 +71,8 @@ struct AppendArgs {
   const void* w_dkv;
   const void* kr_new;
   void* c_out;
-  int32_t batch, d_c, d_r, d_model, row, page_size, max_pages, num_pages;
+  int32_t batch, d_c, d_r, d_model, row, page_size, max_pages, num_pages;  // row: bytes for FP8
+  float cache_inv;  // FP8 caches: fp32 reciprocal of cache_scale
 };
 
 struct CombineArgs {

@@ -10,7 +10,7 @@ namespace mlra {
 
 int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (!d) return MLRA_ERR_INVALID_ARG;
-  if (d->dtype != MLRA_F32 && d->dtype != MLRA_BF16) return MLRA_ERR_UNSUPPORTED;
+  if (d->dtype != MLRA_F32 && d->dtype != MLRA_BF16 && d->dtype != MLRA_FP8_E4M3) return MLRA_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->n_heads < 1 || d->d_h < 1 || d->d_c < 1 || d->n_blocks < 1 ||
       d->blocks_per_head < 1 || d->d_r < 0 || d->max_pages_per_seq < 1 || d->num_pages < 1)
     return MLRA_ERR_INVALID_ARG;
@@ -20,11 +20,15 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (d->n_heads % groups != 0) return MLRA_ERR_INVALID_ARG;
   const int ps = d->page_size;
   if (ps < 16 || ps > 256 || (ps & (ps - 1)) != 0) return MLRA_ERR_INVALID_ARG;
-  const int elem = d->dtype == MLRA_BF16 ? 2 : 4;
+  const int elem = d->dtype == MLRA_F32 ? 4 : 2;
   const int row = d->d_c + d->d_r;
   if ((static_cast<int64_t>(row) * elem) % 16 != 0) return MLRA_ERR_INVALID_ARG;
   const int w = d->d_c / d->n_blocks;
-  if (d->dtype == MLRA_BF16 && (w % 8 != 0 || d->d_r % 8 != 0)) return MLRA_ERR_INVALID_ARG;
+  if (d->dtype != MLRA_F32 && (w % 8 != 0 || d->d_r % 8 != 0)) return MLRA_ERR_INVALID_ARG;
+  // FP8 rows: d_c code bytes in whole 16-byte chunks, then the bf16 RoPE key
+  if (d->dtype == MLRA_FP8_E4M3 && d->d_c % 16 != 0) return MLRA_ERR_INVALID_ARG;
+  if (d->dtype == MLRA_FP8_E4M3 && (!(d->cache_scale == d->cache_scale) || isinf(d->cache_scale)))
+    return MLRA_ERR_INVALID_ARG;
   if (d->dtype == MLRA_F32 && (w % 4 != 0 || d->d_r % 4 != 0)) return MLRA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(d->max_pages_per_seq) * ps > INT32_MAX) return MLRA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(d->batch) * d->max_pages_per_seq > INT32_MAX) return MLRA_ERR_INVALID_ARG;

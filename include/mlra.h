@@ -34,9 +34,17 @@
  *    enqueued on it asynchronously; results are ready when the stream is.
  *  - Element type: every floating-point input (pool, queries, weights, x,
  *    k^R_new, c_out) uses desc->dtype; outputs `out` and `lse` are fp32.
+ *    MLRA_FP8_E4M3 is a quantised cache (the FP8 latent quantisation the
+ *    lesty.tech MLA explainer mentions in section 5): the pool holds the latent
+ *    as OCP FP8 E4M3FN codes, each standing for (decoded code) x cache_scale,
+ *    and the RoPE key in bf16; queries, weights, x and k^R_new are bf16 and
+ *    c_out is fp32. It is supported for the shapes with an MFMA attention
+ *    variant (MLRA_ERR_UNSUPPORTED otherwise).
  *
  * Cache layout (all entry points):
  *  - pool: [num_pages][page_size][d_c + d_r]; row = [c (d_c) | k^R (d_r)].
+ *    MLRA_FP8_E4M3: rows of d_c + 2 d_r bytes, [codes (d_c bytes) | k^R (d_r
+ *    bf16)].
  *  - page_table: int32 [batch][max_pages_per_seq]; token t of sequence b lives
  *    in row page_table[b][t / page_size] * page_size + t % page_size.
  *    NULL means the identity layout: page p of sequence b is
@@ -68,7 +76,7 @@ typedef enum {
   MLRA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } mlra_status;
 
-typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1 } mlra_dtype;
+typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1, MLRA_FP8_E4M3 = 2 } mlra_dtype;
 
 /* Error flags a kernel can raise in the workspace (see mlra_read_flags). */
 #define MLRA_FLAG_BAD_PAGE 1u
@@ -88,6 +96,8 @@ typedef struct {
   int32_t dtype;             /* mlra_dtype */
   float softmax_scale;       /* <= 0 selects 1 / sqrt(d_h + d_r) */
   float out_scale;           /* <= 0 selects 1 / sqrt(blocks_per_head) */
+  float cache_scale;         /* MLRA_FP8_E4M3: latent value of a code = decoded code x
+                                cache_scale (<= 0 selects 1); ignored otherwise */
 } mlra_desc;
 
 /* Bytes of device workspace mlra_decode / mlra_combine need for this shape.
@@ -105,6 +115,10 @@ size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len);
  *   x: [batch][d_model]; w_dkv: [d_model][d_c], 16-byte aligned (else
  *   MLRA_ERR_INVALID_ARG); kr_new: [batch][d_r] (already rotated); positions:
  *   int32 [batch] (device); c_out: [batch][d_c] or NULL.
+ * MLRA_FP8_E4M3: the fp32 latent is multiplied by the fp32 reciprocal of
+ *   cache_scale and encoded to the nearest E4M3FN code (ties to even,
+ *   magnitudes of 448 and above saturate to 448, NaN to 0x7F); c_out receives
+ *   the fp32 latent before encoding.
  * A position outside [0, max_pages_per_seq * page_size) writes nothing. The
  * caller advances its sequence lengths itself. */
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,

@@ -47,7 +47,7 @@ class GpuProblem:
             batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks, d_r=s.d_r,
             max_pages_per_seq=inp.max_pages_per_seq, num_pages=pool_np.shape[0], dtype=s.dtype,
             page_size=s.page_size, blocks_per_head=s.blocks_per_head, d_model=s.d_model,
-            softmax_scale=s.softmax_scale, out_scale=s.out_scale)
+            softmax_scale=s.softmax_scale, out_scale=s.out_scale, cache_scale=s.cache_scale)
         self.max_seq_len = inp.max_seq_len
         self.ws = mlra.alloc_workspace(self.desc, self.max_seq_len)
         self.out = t.empty((s.batch, s.n_heads, s.d_h), dtype=t.float32, device="cuda")
@@ -55,7 +55,8 @@ class GpuProblem:
         if inp.x is not None:
             self.positions = to_dev(inp.positions)
             self.x, self.w_dkv, self.kr_new = to_dev(inp.x), to_dev(inp.w_dkv), to_dev(inp.kr_new)
-            self.c_out = t.empty((s.batch, s.d_c), dtype=self.pool.dtype, device="cuda")
+            c_dtype = t.float32 if s.dtype == "fp8" else self.pool.dtype  # fp8: latent before encoding
+            self.c_out = t.empty((s.batch, s.d_c), dtype=c_dtype, device="cuda")
 
     def append(self, stream=None):
         mlra.append_latent(self.desc, self.pool, self.page_table, self.positions, self.x, self.w_dkv,
@@ -77,13 +78,19 @@ def rms(a):
 
 
 def check_outputs(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out"):
-    """bf16: max |g - r| / RMS(r) <= 2e-2; fp32: max |g - r| / max(|r|, RMS(r)) <= 1e-5."""
+    """bf16: max |g - r| / RMS(r) <= 2e-2; fp8 caches: <= 3e-2;
+    fp32: max |g - r| / max(|r|, RMS(r)) <= 1e-5."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
     r = rms(ref)
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp8"):
+        # fp8 caches compute exactly like the bf16 path (bf16 q~ and P, fp32
+        # accumulation); their bar is what those two roundings produce on the
+        # fp8 test inputs: a numpy emulation of just those roundings reaches
+        # 2.7e-2 of the RMS on the worst case, so the bar is 3e-2
+        tol = 2e-2 if dtype == "bf16" else 3e-2
         err = float(np.max(np.abs(gpu - ref))) / max(r, 1e-30)
-        assert err <= 2e-2, f"{what}: max err / rms = {err:.3e}"
+        assert err <= tol, f"{what}: max err / rms = {err:.3e}"
     else:
         err = float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), r)))
         assert err <= 1e-5, f"{what}: max rel err = {err:.3e}"
@@ -96,5 +103,5 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, dtype: str):
     assert np.all(gpu[~finite] == ref[~finite])
     if finite.any():
         d = np.abs(gpu[finite] - ref[finite])
-        tol = 5e-2 if dtype == "bf16" else 1e-5 * max(1.0, float(np.max(np.abs(ref[finite]))))
+        tol = 5e-2 if dtype in ("bf16", "fp8") else 1e-5 * max(1.0, float(np.max(np.abs(ref[finite]))))
         assert float(np.max(d)) <= tol, f"lse: max abs err {float(np.max(d)):.3e}"

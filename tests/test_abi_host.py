@@ -169,3 +169,16 @@ def test_stream_read_validation():
     assert L.mlra_stream_read(FAKE, 1024, None, 1 << 20, None) == mlra.ERR_INVALID_ARG
     assert L.mlra_stream_read(FAKE, 1000, FAKE, 1 << 20, None) == mlra.ERR_INVALID_ARG  # not a multiple of 16
     assert L.mlra_stream_read(FAKE, 1024, FAKE, 4, None) == mlra.ERR_INVALID_ARG        # sink too small
+
+
+def test_fp8_needs_an_mfma_variant_and_aligned_rows():
+    """FP8 caches run on the MFMA variants only; other shapes are rejected
+    before any launch, as are rows that are not whole 16-byte chunks."""
+    ok = _desc(dtype="fp8", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, cache_scale=0.5)
+    assert mlra.lib().mlra_workspace_bytes(ctypes.byref(ok), 10) > 0
+    no_variant = _desc(dtype="fp8", n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16)
+    assert _decode(no_variant) == mlra.ERR_UNSUPPORTED
+    bad_row = _desc(dtype="fp8", n_heads=8, d_h=16, d_c=72, n_blocks=1, d_r=16)
+    assert _decode(bad_row) == mlra.ERR_INVALID_ARG
+    nan_scale = _desc(dtype="fp8", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, cache_scale=float("nan"))
+    assert _decode(nan_scale) == mlra.ERR_INVALID_ARG

@@ -273,3 +273,70 @@ def test_graph_replay_matches_eager():
         junk.mul_(2.0).sum().item()
         prob.step()
         t.cuda.synchronize()
+
+
+
+# ------------------------------------------------------------------ FP8 cache
+
+FP8_SHAPES = {
+    # same head/latent structure as the bf16 workloads, E4M3FN latent codes
+    "mlra4": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8", cache_scale=0.5),
+              [1, 33, 64, 650]),
+    "mla": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="fp8", cache_scale=0.25), [31, 96]),
+    "tp_share": (dict(n_heads=16, d_h=128, d_c=128, n_blocks=1, d_r=64, dtype="fp8", cache_scale=1.0),
+                 [5, 129, 900, 2049]),
+    "mlra2": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="fp8", cache_scale=1.25),
+              [100, 0, 333]),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_SHAPES))
+def test_fp8_small_all_outputs(name):
+    """FP8 caches against the oracle on the same codes (every output and lse;
+    NaN canaries in unused rows)."""
+    kw, lens = FP8_SHAPES[name]
+    _say(f"case: fp8 {name}, lengths {lens}")
+    s = synth.Shape(batch=len(lens), **kw)
+    inp = synth.make_inputs(s, ("list", lens), 4200 + len(name))
+    _, err = _run_and_compare(inp)
+    _say(f"fp8 {name}: max err/rms {err:.2e}")
+
+
+def test_fp8_full_size_sampled():
+    _say("case: full-size fp8 workload (MLRA-4 shape, B=32, 8K)")
+    inp = synth.workload_inputs(6)
+    rng = np.random.default_rng(6)
+    s = inp.shape
+    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
+    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
+    _, err = _run_and_compare(inp, pairs)
+    _say(f"fp8 full: max err/rms {err:.2e}")
+
+
+def test_fp8_append_encodes_kernel_latent():
+    """FP8 append: the fp32 latent (c_out) matches the oracle's to the fp32 bar,
+    every code is bit-identical to the oracle's encoding of that same fp32
+    latent times the reciprocal scale, the RoPE key lands as bf16 and no
+    other byte changes."""
+    _say("case: fp8 append")
+    s = synth.Shape(batch=5, n_heads=8, d_h=32, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
+                    cache_scale=0.125, d_model=1000)
+    inp = synth.make_inputs(s, ("list_append", [0, 63, 64, 127, 500]), 78)
+    prob = _gpu.GpuProblem(inp)
+    before = prob.pool.cpu().numpy().copy()
+    prob.append()
+    after = prob.pool.cpu().numpy()
+    c_gpu = prob.c_out.cpu().numpy()
+    pool_ref = inp.pool.copy()
+    c_ref = oracle.append(inp, pool_ref)
+    err = np.abs(c_gpu.astype(np.float64) - c_ref) / np.maximum(np.abs(c_ref), _gpu.rms(c_ref))
+    assert err.max() <= 1e-5, err.max()
+    codes_want = oracle.e4m3_encode_array(c_gpu * np.float32(1.0 / 0.125))
+    changed = np.zeros(before.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // 64], pos % 64
+        changed[pg, off] = True
+        assert np.array_equal(after[pg, off, :s.d_c], codes_want[b])
+        assert np.array_equal(after[pg, off, s.d_c:].view(np.uint16), inp.kr_new[b])
+    assert np.array_equal(before[~changed], after[~changed])
