@@ -36,7 +36,14 @@ HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8K, 1 GPU"
 KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_mfma_mlra4_b32_ctx8k_counters.txt")
+# rocprofv3 counter summaries of the attention kernel, per workload
+PROFILE_TAGS = {2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
+                5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k"}
+
+
+def _counters_file(workload: int) -> str:
+    tag = PROFILE_TAGS.get(workload, "none")
+    return os.path.join(ROOT, "profiles", f"attend_mfma_{tag}_counters.txt")
 COPY_BYTES = 1 << 30
 
 
@@ -45,7 +52,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,12 +81,14 @@ def _source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def _traffic(bytes_alg: float):
+def _traffic(bytes_alg: float, workload: int):
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
-    counter summary, when it was taken on the current kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
+    counter summary of this workload, when it was taken on the current kernel
+    source."""
+    path = _counters_file(workload)
+    if not os.path.exists(path):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(path).read()
     m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
     if not m or m.group(1) != _source_hash():
         return None
@@ -133,7 +142,7 @@ def main():
     desc = mlra.make_desc(batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
                           d_r=s.d_r, max_pages_per_seq=inp.max_pages_per_seq,
                           num_pages=pools_np[0].shape[0], dtype=s.dtype, page_size=s.page_size,
-                          blocks_per_head=s.blocks_per_head, d_model=s.d_model)
+                          blocks_per_head=s.blocks_per_head, d_model=s.d_model, cache_scale=s.cache_scale)
     ws = mlra.alloc_workspace(desc, inp.max_seq_len)
     out = torch.empty((s.batch, s.n_heads, s.d_h), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -210,9 +219,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": s.dtype,
+        "dtype": "f32" if s.dtype == "f32" else "bf16",  # fp8 caches compute in bf16
         "data": "synthetic",
-        "config": {"workload": wl["name"], "workload_id": args.workload, "batch": s.batch, "n_heads": s.n_heads, "d_h": s.d_h,
+        "config": {"workload": wl["name"], "workload_id": args.workload, "cache_dtype": s.dtype, "batch": s.batch, "n_heads": s.n_heads, "d_h": s.d_h,
                    "d_c": s.d_c, "n_blocks": s.n_blocks, "d_r": s.d_r, "page_size": s.page_size,
                    "context_tokens": n_tokens, "heads_per_block": heads_per_block,
                    "pool_instances": len(pools), "parallelism": "single GPU"},
@@ -239,7 +248,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes_per_launch": cache_bytes,
             "algorithmic_flops_per_launch": attn_flops,
-            "traffic": _traffic(cache_bytes),
+            "traffic": _traffic(cache_bytes, args.workload),
             "mfma_tflops": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12, 2),
             "mfma_frac_of_bf16_peak": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         },
@@ -255,8 +264,7 @@ def _cache_bytes(inp, s):
     """Algorithmic cache bytes of one step: every attended token's row once
     (k^R is read once for all blocks)."""
     import numpy as np
-    elem = 2 if s.dtype == "bf16" else 4
-    return float(np.sum(inp.seq_lens.astype(np.int64))) * (s.d_c + s.d_r) * elem
+    return float(np.sum(inp.seq_lens.astype(np.int64))) * s.row_bytes
 
 
 def _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk, w_uv, ws, desc, out, stream,
