@@ -30,6 +30,7 @@ class OracleShape(ctypes.Structure):
         ("d_model", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double), ("out_scale", ctypes.c_double),
         ("cache_scale", ctypes.c_double),
+        ("d_cq", ctypes.c_int32), ("rope_base", ctypes.c_double),
     ]
 
 
@@ -66,6 +67,12 @@ def lib():
         L.oracle_row_index.restype = ctypes.c_int64
         L.oracle_round_bf16.argtypes = [ctypes.c_double]
         L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_rope.argtypes = [dp, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]
+        L.oracle_rope.restype = None
+        L.oracle_rope_key.argtypes = [sp, vp, vp, ip, dp]
+        L.oracle_rope_key.restype = None
+        L.oracle_project_query.argtypes = [sp, vp, vp, vp, vp, ip, dp, dp]
+        L.oracle_project_query.restype = None
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
@@ -91,7 +98,8 @@ def shape_of(inp, softmax_scale: Optional[float] = None, out_scale: Optional[flo
         dtype={"bf16": BF16, "f32": F32, "fp8": FP8}[s.dtype],
         softmax_scale=s.softmax_scale if softmax_scale is None else softmax_scale,
         out_scale=s.out_scale if out_scale is None else out_scale,
-        cache_scale=getattr(s, "cache_scale", 0.0))
+        cache_scale=getattr(s, "cache_scale", 0.0), d_cq=getattr(s, "d_cq", 0),
+        rope_base=getattr(s, "rope_base", 0.0))
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -170,6 +178,34 @@ def row_index(inp, b: int, t: int, page_table=None) -> int:
 
 def round_bf16(v: float) -> int:
     return int(lib().oracle_round_bf16(float(v)))
+
+
+def rope(v: np.ndarray, pos: int, base: float = 10000.0) -> np.ndarray:
+    """RoPE of one vector (a rotated copy)."""
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    lib().oracle_rope(out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), out.size, int(pos), float(base))
+    return out
+
+
+def rope_key(inp) -> np.ndarray:
+    """k^R [B][d_r] for the new token of every sequence (inp.w_kr, inp.positions)."""
+    s = inp.shape
+    out = np.zeros((s.batch, s.d_r))
+    lib().oracle_rope_key(ctypes.byref(shape_of(inp)), _ptr(inp.x), _ptr(inp.w_kr), _iptr(inp.positions),
+                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return out
+
+
+def project_query(inp):
+    """(q^C [B][h][d_h], q^R [B][h][d_r]) from x and the query-path weights."""
+    s = inp.shape
+    qc = np.zeros((s.batch, s.n_heads, s.d_h))
+    qr = np.zeros((s.batch, s.n_heads, s.d_r))
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib().oracle_project_query(ctypes.byref(shape_of(inp)), _ptr(inp.x), _ptr(inp.w_dq), _ptr(inp.w_uq),
+                               _ptr(inp.w_qr), _iptr(inp.positions), qc.ctypes.data_as(dp),
+                               qr.ctypes.data_as(dp))
+    return qc, qr
 
 
 def e4m3_decode(code: int) -> float:

@@ -328,6 +328,65 @@ void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
   }
 }
 
+/* ------------------------------------------------ RoPE and the query path */
+
+static double rope_base_of(const oracle_shape* s) { return s->rope_base > 0 ? s->rope_base : 10000.0; }
+
+void oracle_rope(double* v, int32_t d, int32_t pos, double base) {
+  for (int32_t i = 0; i < d / 2; ++i) {
+    const double theta = pow(base, -2.0 * i / d);
+    const double a = (double)pos * theta, c = cos(a), sn = sin(a);
+    const double x0 = v[2 * i], x1 = v[2 * i + 1];
+    v[2 * i] = x0 * c - x1 * sn;
+    v[2 * i + 1] = x0 * sn + x1 * c;
+  }
+}
+
+void oracle_rope_key(const oracle_shape* s, const void* x, const void* w_kr, const int32_t* positions,
+                     double* kr_out) {
+  const int32_t DM = s->d_model, DR = s->d_r, dt = arrays_dtype(s);
+  for (int32_t b = 0; b < s->batch; ++b) {
+    double* k = kr_out + (int64_t)b * DR;
+    for (int32_t r = 0; r < DR; ++r) { /* h W^KR, W^KR stored [d_model][d_r] */
+      double v = 0.0;
+      for (int32_t m = 0; m < DM; ++m) v += elem(dt, x, (int64_t)b * DM + m) * elem(dt, w_kr, (int64_t)m * DR + r);
+      k[r] = v;
+    }
+    oracle_rope(k, DR, positions[b], rope_base_of(s));
+  }
+}
+
+void oracle_project_query(const oracle_shape* s, const void* x, const void* w_dq, const void* w_uq,
+                          const void* w_qr, const int32_t* positions, double* q_c_out,
+                          double* q_r_out) {
+  const int32_t DM = s->d_model, DQ = s->d_cq, H = s->n_heads, DH = s->d_h, DR = s->d_r;
+  const int32_t dt = arrays_dtype(s);
+  double* cq = (double*)malloc(sizeof(double) * (size_t)DQ);
+  for (int32_t b = 0; b < s->batch; ++b) {
+    for (int32_t c = 0; c < DQ; ++c) { /* c^Q = h W^DQ */
+      double v = 0.0;
+      for (int32_t m = 0; m < DM; ++m) v += elem(dt, x, (int64_t)b * DM + m) * elem(dt, w_dq, (int64_t)m * DQ + c);
+      cq[c] = v;
+    }
+    for (int32_t i = 0; i < H; ++i) {
+      double* qc = q_c_out + ((int64_t)b * H + i) * DH;
+      double* qr = q_r_out + ((int64_t)b * H + i) * DR;
+      for (int32_t d = 0; d < DH; ++d) { /* q^C_i = c^Q W^UQ_i */
+        double v = 0.0;
+        for (int32_t c = 0; c < DQ; ++c) v += cq[c] * elem(dt, w_uq, ((int64_t)i * DQ + c) * DH + d);
+        qc[d] = v;
+      }
+      for (int32_t r = 0; r < DR; ++r) { /* q^R_i = RoPE(c^Q W^QR_i) */
+        double v = 0.0;
+        for (int32_t c = 0; c < DQ; ++c) v += cq[c] * elem(dt, w_qr, ((int64_t)i * DQ + c) * DR + r);
+        qr[r] = v;
+      }
+      oracle_rope(qr, DR, positions[b], rope_base_of(s));
+    }
+  }
+  free(cq);
+}
+
 /* --------------------------------------------------------------- counters */
 
 double oracle_cache_elems_per_token(int32_t method, int32_t h, int32_t d_h, int32_t g,

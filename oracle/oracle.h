@@ -46,6 +46,8 @@ typedef struct {
   double softmax_scale;    /* <= 0 selects 1 / sqrt(d_h + d_r) */
   double out_scale;        /* <= 0 selects 1 / sqrt(blocks_per_head) */
   double cache_scale;      /* FP8 caches: scale of every latent code (<= 0 selects 1) */
+  int32_t d_cq;            /* query path: width of the query latent c^Q */
+  double rope_base;        /* RoPE base (<= 0 selects 10000) */
 } oracle_shape;
 
 /* Block attended by head `head` in its `jj`-th slot (0 <= jj < k). */
@@ -88,6 +90,26 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
 void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
                    const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
                    void* c_out);
+
+/* Rotary position embedding (RoFormer, cited by the MLRA index page; the
+ * lesty.tech explainer's section 4 applies it to the decoupled key and query):
+ * pairs (v[2i], v[2i+1]) of a d-wide vector rotate by the angle pos theta_i,
+ * theta_i = base^(-2i/d). In place, d even. */
+void oracle_rope(double* v, int32_t d, int32_t pos, double base);
+
+/* The steps on either side of the attention (lesty.tech section 4; MLA's
+ * query compression), for the token at positions[b]:
+ *   k^R[b] = RoPE(x[b] W^KR)                       W^KR: [d_model][d_r]
+ *   c^Q[b] = x[b] W^DQ                             W^DQ: [d_model][d_cq]
+ *   q^C[b][i] = c^Q[b] W^UQ[i]                     W^UQ: [h][d_cq][d_h]
+ *   q^R[b][i] = RoPE(c^Q[b] W^QR[i])               W^QR: [h][d_cq][d_r]
+ * in double; arrays use the shape's array encoding; outputs are doubles
+ * (kr_out [batch][d_r], q_c_out [batch][h][d_h], q_r_out [batch][h][d_r]). */
+void oracle_rope_key(const oracle_shape* s, const void* x, const void* w_kr, const int32_t* positions,
+                     double* kr_out);
+void oracle_project_query(const oracle_shape* s, const void* x, const void* w_dq, const void* w_uq,
+                          const void* w_qr, const int32_t* positions, double* q_c_out,
+                          double* q_r_out);
 
 /* Rounds a double to a bf16 bit pattern, nearest with ties to even. */
 uint16_t oracle_round_bf16(double v);

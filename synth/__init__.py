@@ -12,7 +12,10 @@ Recipe (one generator per call, numpy Philox keyed by the seed, fixed order):
   4. q^C [B][h][d_h] and q^R [B][h][d_r], N(0, 1);
   5. W^UK and W^UV [h][k][w][d_h], N(0, 1) / sqrt(w) (w = latent block width);
   6. append only: x [B][d_model] N(0, 1), W^DKV [d_model][d_c] N(0, 1) /
-     sqrt(d_model), k^R_new [B][d_r] N(0, 1).
+     sqrt(d_model), k^R_new [B][d_r] N(0, 1);
+  7. append with a query width d_cq > 0 only (the steps on either side of the
+     attention): W^KR [d_model][d_r] and W^DQ [d_model][d_cq] N(0, 1) /
+     sqrt(d_model), W^UQ [h][d_cq][d_h] and W^QR [h][d_cq][d_r] N(0, 1) / sqrt(d_cq).
 Rows of the pool that hold no token (the tail of each sequence's last page, a
 spare page per sequence for the append target, and one guard page that unused
 page-table entries point at) are filled with a NaN canary so that a kernel that
@@ -20,8 +23,9 @@ reads outside the sequence shows up as NaN in its outputs.
 
 FP8 caches (dtype "fp8"): a row is d_c bytes of OCP E4M3FN codes followed by the
 RoPE key as d_r bf16 values. Step 3 then draws each code's fields directly as
-integers (sign uniform in {0, 1}, exponent field uniform in 4..9, mantissa field
-uniform in 0..7: magnitudes between 1/8 and 7.5, no zeros or NaN) and the RoPE
+integers (sign uniform in {0, 1}, exponent field uniform in 3..7, mantissa field
+uniform in 0..7: magnitudes between 1/16 and 1.875, RMS about 0.8 like the
+N(0, 1) latents of the bf16 workloads; no zeros or NaN) and the RoPE
 key N(0, 1) in bf16; every other array is bf16. The NaN canary is code 0x7F and
 the bf16 NaN.
 """
@@ -53,6 +57,8 @@ class Shape:
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_h + d_r)
     out_scale: float = 0.0  # 0 -> 1/sqrt(blocks_per_head)
     cache_scale: float = 0.0  # fp8: latent value = decoded code x cache_scale (0 -> 1)
+    d_cq: int = 0  # query-path width (0: no query-path weights drawn)
+    rope_base: float = 0.0  # RoPE base (0 -> 10000)
 
     @property
     def w(self) -> int:
@@ -98,9 +104,9 @@ WORKLOADS = {
                         d_model=4096),
             lengths=("uniform_append", 1024, 131072)),
     # the FP8 latent cache of the next-step list: workload 2's shape with E4M3FN codes
-    6: dict(name="MLRA-4 fp8-e4m3 cache (scale 0.5), B=32 h=64 d_h=128 d_c=512(4x128) d_r=64 ctx=8192 paged",
+    6: dict(name="MLRA-4 fp8-e4m3 cache (scale 1.25), B=32 h=64 d_h=128 d_c=512(4x128) d_r=64 ctx=8192 paged",
             shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
-                        cache_scale=0.5),
+                        cache_scale=1.25),
             lengths=("fixed", 8192)),
 }
 
@@ -146,6 +152,11 @@ class Inputs:
     x: Optional[np.ndarray] = None
     w_dkv: Optional[np.ndarray] = None
     kr_new: Optional[np.ndarray] = None
+    # query path and RoPE key (None unless the shape has d_cq > 0)
+    w_kr: Optional[np.ndarray] = None
+    w_dq: Optional[np.ndarray] = None
+    w_uq: Optional[np.ndarray] = None
+    w_qr: Optional[np.ndarray] = None
 
     @property
     def max_seq_len(self) -> int:
@@ -156,7 +167,7 @@ def _fp8_pool(rng: np.random.Generator, pages_rows, d_c: int, d_r: int) -> np.nd
     """FP8 cache rows: E4M3FN code fields drawn as integers, then the bf16 RoPE key."""
     size = tuple(pages_rows) + (d_c,)
     sign = rng.integers(0, 2, size=size, dtype=np.uint8)
-    expo = rng.integers(4, 10, size=size, dtype=np.uint8)
+    expo = rng.integers(3, 8, size=size, dtype=np.uint8)
     mant = rng.integers(0, 8, size=size, dtype=np.uint8)
     rope = _normal(rng, tuple(pages_rows) + (d_r,), 1.0, "bf16")
     pool = np.empty(tuple(pages_rows) + (d_c + 2 * d_r,), dtype=np.uint8)
@@ -264,6 +275,12 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
         inp.x = _normal(rng, (B, DM), 1.0, adt)
         inp.w_dkv = _normal(rng, (DM, shape.d_c), 1.0 / math.sqrt(DM), adt)
         inp.kr_new = _normal(rng, (B, DR), 1.0, adt)
+        if shape.d_cq > 0:
+            DQ = shape.d_cq
+            inp.w_kr = _normal(rng, (DM, DR), 1.0 / math.sqrt(DM), adt)
+            inp.w_dq = _normal(rng, (DM, DQ), 1.0 / math.sqrt(DM), adt)
+            inp.w_uq = _normal(rng, (H, DQ, DH), 1.0 / math.sqrt(DQ), adt)
+            inp.w_qr = _normal(rng, (H, DQ, DR), 1.0 / math.sqrt(DQ), adt)
     return inp
 
 

@@ -578,3 +578,68 @@ def test_fp8_append_encodes_the_fp32_latent():
         assert np.array_equal(pool[pg, off, :s.d_c], want[b])
         assert np.array_equal(pool[pg, off, s.d_c:].view(np.uint16), inp.kr_new[b])
     assert np.array_equal(pool[~changed], inp.pool[~changed])
+
+
+# ------------------------------------------------- RoPE and the query path
+# lesty.tech section 4: k^R = RoPE(h W^KR), the query split the same way; the
+# rotation is RoFormer's (cited by the MLRA index page). Readings in the design notes.
+
+def test_rope_closed_forms():
+    # position 0 is the identity
+    v = np.random.default_rng(1).standard_normal(64)
+    assert np.array_equal(oracle.rope(v, 0), v)
+    # d = 2: theta_0 = 1, so (1, 0) turns by pos radians, counter-clockwise
+    for pos in (1, 2, 7, 1000):
+        r = oracle.rope(np.array([1.0, 0.0]), pos)
+        assert abs(r[0] - math.cos(pos)) < 1e-12 and abs(r[1] - math.sin(pos)) < 1e-12
+    # d = 4, base 10000: pair 1 turns at 10000^(-1/2) = 0.01 rad per position
+    r = oracle.rope(np.array([0.0, 0.0, 0.0, 1.0]), 100)
+    assert np.allclose(r, [0.0, 0.0, -math.sin(1.0), math.cos(1.0)], atol=1e-12)
+    # adjacent pairs: a unit vector stays inside its own pair
+    e1 = np.zeros(8)
+    e1[5] = 1.0
+    r = oracle.rope(e1, 33)
+    assert np.all(r[[0, 1, 2, 3, 6, 7]] == 0.0) and abs(np.hypot(r[4], r[5]) - 1.0) < 1e-12
+    # another base
+    r = oracle.rope(np.array([0.0, 0.0, 1.0, 0.0]), 10, base=100.0)
+    assert np.allclose(r, [0.0, 0.0, math.cos(1.0), math.sin(1.0)], atol=1e-12)
+
+
+def test_rope_is_a_rotation_with_relative_positions():
+    """Norms are preserved and <RoPE(q, m), RoPE(k, n)> depends only on m - n
+    (RoFormer's defining property)."""
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m in (0, 5, 1234):
+        assert abs(np.linalg.norm(oracle.rope(q, m)) - np.linalg.norm(q)) < 1e-10
+    base = float(oracle.rope(q, 40) @ oracle.rope(k, 25))
+    for shift in (1, 17, 9000):
+        assert abs(float(oracle.rope(q, 40 + shift) @ oracle.rope(k, 25 + shift)) - base) < 1e-9
+    assert abs(float(oracle.rope(q, 15) @ oracle.rope(k, 0)) - base) < 1e-9
+
+
+def _proj_inputs(dtype="f32", seed=31):
+    s = synth.Shape(batch=3, n_heads=4, d_h=16, d_c=64, n_blocks=4, d_r=16, dtype=dtype, d_model=48,
+                    d_cq=24, rope_base=500.0)
+    return synth.make_inputs(s, ("list_append", [0, 70, 300]), seed)
+
+
+def test_rope_key_is_rotated_projection():
+    inp = _proj_inputs()
+    kr = oracle.rope_key(inp)
+    xw = _f(inp.x) @ _f(inp.w_kr)  # numpy matmul
+    for b in range(inp.shape.batch):
+        assert np.allclose(kr[b], oracle.rope(xw[b], int(inp.positions[b]), base=500.0), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_project_query_against_numpy(dtype):
+    inp = _proj_inputs(dtype)
+    qc, qr = oracle.project_query(inp)
+    cq = _f(inp.x) @ _f(inp.w_dq)
+    s = inp.shape
+    for b in range(s.batch):
+        for i in range(s.n_heads):
+            assert np.allclose(qc[b, i], cq[b] @ _f(inp.w_uq)[i], rtol=1e-12, atol=1e-12)
+            want = oracle.rope(cq[b] @ _f(inp.w_qr)[i], int(inp.positions[b]), base=500.0)
+            assert np.allclose(qr[b, i], want, rtol=1e-12, atol=1e-12)
