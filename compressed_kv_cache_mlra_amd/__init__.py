@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmlra.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class MlraError(RuntimeError):
@@ -41,20 +41,20 @@ class MlraDesc(ctypes.Structure):
         ("d_r", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32), ("d_model", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("out_scale", ctypes.c_float),
-        ("cache_scale", ctypes.c_float),
+        ("cache_scale", ctypes.c_float), ("d_cq", ctypes.c_int32), ("rope_base", ctypes.c_float),
     ]
 
 
 def make_desc(batch, n_heads, d_h, d_c, n_blocks, d_r, max_pages_per_seq, num_pages, dtype,
               page_size=64, blocks_per_head=1, d_model=0, softmax_scale=0.0, out_scale=0.0,
-              cache_scale=0.0) -> MlraDesc:
+              cache_scale=0.0, d_cq=0, rope_base=0.0) -> MlraDesc:
     if isinstance(dtype, str):
         dtype = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}[dtype]
     return MlraDesc(batch=batch, n_heads=n_heads, d_h=d_h, d_c=d_c, n_blocks=n_blocks,
                     blocks_per_head=blocks_per_head, d_r=d_r, page_size=page_size,
                     max_pages_per_seq=max_pages_per_seq, num_pages=num_pages, d_model=d_model,
                     dtype=dtype, softmax_scale=softmax_scale, out_scale=out_scale,
-                    cache_scale=cache_scale)
+                    cache_scale=cache_scale, d_cq=d_cq, rope_base=rope_base)
 
 
 _lib = None
@@ -80,8 +80,11 @@ def lib() -> ctypes.CDLL:
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
         L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+        L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp]
+        L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp]
         for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
-                  "mlra_combine", "mlra_read_flags", "mlra_stream_read"):
+                  "mlra_combine", "mlra_read_flags", "mlra_stream_read", "mlra_rope_key",
+                  "mlra_project_query"):
             getattr(L, f).restype = ctypes.c_int
         if L.mlra_abi_version() != ABI_VERSION:
             raise ImportError("libmlra ABI version mismatch; rebuild the library")
@@ -188,6 +191,35 @@ def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=Non
         (_ptr(c_out, kind="f32", name="c_out", numel=B * desc.d_c, nullable=True) if desc.dtype == FP8_E4M3
          else _ptr(c_out, desc, name="c_out", numel=B * desc.d_c, nullable=True)),
         _stream(stream)), "append_latent")
+
+
+def rope_key(desc, x, w_kr, positions, kr_out, stream=None):
+    """kr_out[b] = RoPE(x[b] W^KR, positions[b]) (feeds append_latent's kr_new)."""
+    B = desc.batch
+    _check(lib().mlra_rope_key(
+        ctypes.byref(desc),
+        _ptr(x, desc, name="x", numel=B * desc.d_model),
+        _ptr(w_kr, desc, name="w_kr", numel=desc.d_model * desc.d_r),
+        _ptr(positions, kind="int32", name="positions", numel=B),
+        _ptr(kr_out, desc, name="kr_out", numel=B * desc.d_r),
+        _stream(stream)), "rope_key")
+
+
+def project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, stream=None):
+    """c_q = x W^DQ (fp32), q_c[:, i] = c_q W^UQ[i], q_r[:, i] = RoPE(c_q W^QR[i])."""
+    B, H, DQ = desc.batch, desc.n_heads, desc.d_cq
+    no_r = desc.d_r == 0
+    _check(lib().mlra_project_query(
+        ctypes.byref(desc),
+        _ptr(x, desc, name="x", numel=B * desc.d_model),
+        _ptr(w_dq, desc, name="w_dq", numel=desc.d_model * DQ),
+        _ptr(w_uq, desc, name="w_uq", numel=H * DQ * desc.d_h),
+        _ptr(w_qr, desc, name="w_qr", numel=H * DQ * desc.d_r, nullable=no_r),
+        _ptr(positions, kind="int32", name="positions", numel=B, nullable=no_r),
+        _ptr(c_q, kind="f32", name="c_q", numel=B * DQ),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=no_r),
+        _stream(stream)), "project_query")
 
 
 def absorb_query(desc, seq_lens, q_c, q_r, w_uk, workspace, stream=None):

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmlra.so")
 ARCH = os.environ.get("MLRA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "validate.cpp", "absorb.hip", "attend_mfma.hip", "attend_generic.hip",
-           "combine.hip", "append.hip", "stream_read.hip"]
+           "combine.hip", "append.hip", "stream_read.hip", "proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -134,7 +134,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 2; }
+int mlra_abi_version(void) { return 3; }
 
 const char* mlra_status_string(int status) {
   switch (status) {

@@ -87,6 +87,23 @@ struct CombineArgs {
   float out_scale;
 };
 
+// y[b][m][n] = sum_k x[b][k] W_m[k][n] (+ RoPE on each output vector).
+struct ProjArgs {
+  const void* x;
+  int64_t x_bstride;   // elements between sequences of x
+  int32_t x_f32;       // x is fp32 (else bf16)
+  const void* w;
+  int64_t w_mstride;   // elements between the matrices W_m
+  int32_t w_bf16;      // W is bf16 (else fp32)
+  void* y;
+  int64_t y_bstride, y_mstride;
+  int32_t y_bf16;      // y is bf16 (else fp32)
+  int32_t B, K, N;     // N a multiple of 8
+  const int32_t* positions;
+  int32_t rope;
+  float rope_base;
+};
+
 // ------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {

@@ -33,4 +33,7 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 
 hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t stream);
 
+// n_mats matrices W_m share one launch (the heads of a per-head projection).
+hipError_t launch_proj(const ProjArgs& a, int n_mats, hipStream_t stream);
+
 }  // namespace mlra

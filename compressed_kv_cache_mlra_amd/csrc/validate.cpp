@@ -35,6 +35,7 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (!(d->softmax_scale == d->softmax_scale) || !(d->out_scale == d->out_scale) ||
       isinf(d->softmax_scale) || isinf(d->out_scale))
     return MLRA_ERR_INVALID_ARG;
+  if (d->d_cq < 0 || !(d->rope_base == d->rope_base) || isinf(d->rope_base)) return MLRA_ERR_INVALID_ARG;
   // Kernel limits of this build.
   if (d->batch > kMaxBatch) return MLRA_ERR_UNSUPPORTED;
   if (d->d_h > 512 || d->d_r > 512 || w > 512) return MLRA_ERR_UNSUPPORTED;

@@ -98,6 +98,8 @@ typedef struct {
   float out_scale;           /* <= 0 selects 1 / sqrt(blocks_per_head) */
   float cache_scale;         /* MLRA_FP8_E4M3: latent value of a code = decoded code x
                                 cache_scale (<= 0 selects 1); ignored otherwise */
+  int32_t d_cq;              /* mlra_project_query only: query latent width d_c' */
+  float rope_base;           /* RoPE frequency base (<= 0 selects 10000) */
 } mlra_desc;
 
 /* Bytes of device workspace mlra_decode / mlra_combine need for this shape.
@@ -162,6 +164,36 @@ int mlra_decode(const mlra_desc* desc, const void* pool, const int32_t* page_tab
  *   w_uv: [h][k][w][d_h]. */
 int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, const void* w_uv,
                  float* out, float* lse, void* stream);
+
+/* RoPE key of the new token (the decoupled key of lesty.tech section 4,
+ * computed from the token's hidden state and rotated for its position):
+ *   kr_out[b] = RoPE(x[b] W^KR, positions[b]),  W^KR stored [d_model][d_r].
+ * RoPE (RoFormer's rotary embedding): coordinates (2i, 2i+1) of a d-wide
+ * vector turn by the angle pos * rope_base^(-2i / d), i = 0 .. d/2 - 1.
+ * The product is accumulated in fp32, the angles are evaluated in fp64 and
+ * the rotated value is rounded once to the element type.
+ *   x: [batch][d_model]; w_kr: 16-byte aligned; positions: int32 [batch]
+ *   (device); kr_out: [batch][d_r], ready to be passed to mlra_append_latent
+ *   as kr_new. Element type: desc->dtype (bf16 for MLRA_FP8_E4M3).
+ * d_r == 0 does nothing; d_r % 8 != 0 is MLRA_ERR_UNSUPPORTED. */
+int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
+                  const int32_t* positions, void* kr_out, void* stream);
+
+/* The query path (lesty.tech section 4: the query is compressed and split like
+ * the key; MLA's parameter count on the "Multi-Head Low-Rank Attention" paper
+ * page, thelatestinai.com, lists W^DQ, W^UQ and W^QR):
+ *   c_q[b]     = x[b] W^DQ                   (fp32 [batch][d_cq], W^DQ [d_model][d_cq])
+ *   q_c[b][i]  = c_q[b] W^UQ[i]              ([batch][h][d_h], W^UQ [h][d_cq][d_h])
+ *   q_r[b][i]  = RoPE(c_q[b] W^QR[i], positions[b])  ([batch][h][d_r], W^QR [h][d_cq][d_r])
+ * c_q is caller-owned device memory that receives the unrounded fp32
+ * compressed query and is read back by the second and third products; q_c
+ * and q_r are rounded once to the element type (desc->dtype, bf16 for
+ * MLRA_FP8_E4M3) and feed mlra_absorb_query / mlra_decode directly.
+ * Weights 16-byte aligned; d_cq, d_h and d_r multiples of 8 (else
+ * MLRA_ERR_UNSUPPORTED); with d_r == 0, w_qr, q_r and positions may be NULL. */
+int mlra_project_query(const mlra_desc* desc, const void* x, const void* w_dq, const void* w_uq,
+                       const void* w_qr, const int32_t* positions, float* c_q, void* q_c,
+                       void* q_r, void* stream);
 
 /* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host memory),
  * after the work already enqueued on `stream` (synchronises it). The flags are

@@ -47,7 +47,8 @@ class GpuProblem:
             batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks, d_r=s.d_r,
             max_pages_per_seq=inp.max_pages_per_seq, num_pages=pool_np.shape[0], dtype=s.dtype,
             page_size=s.page_size, blocks_per_head=s.blocks_per_head, d_model=s.d_model,
-            softmax_scale=s.softmax_scale, out_scale=s.out_scale, cache_scale=s.cache_scale)
+            softmax_scale=s.softmax_scale, out_scale=s.out_scale, cache_scale=s.cache_scale,
+            d_cq=s.d_cq, rope_base=s.rope_base)
         self.max_seq_len = inp.max_seq_len
         self.ws = mlra.alloc_workspace(self.desc, self.max_seq_len)
         self.out = t.empty((s.batch, s.n_heads, s.d_h), dtype=t.float32, device="cuda")

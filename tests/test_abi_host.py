@@ -182,3 +182,39 @@ def test_fp8_needs_an_mfma_variant_and_aligned_rows():
     assert _decode(bad_row) == mlra.ERR_INVALID_ARG
     nan_scale = _desc(dtype="fp8", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, cache_scale=float("nan"))
     assert _decode(nan_scale) == mlra.ERR_INVALID_ARG
+
+
+def test_rope_key_validation():
+    L = mlra.lib()
+    d = _desc(d_model=64)
+
+    def call(desc=d, x=FAKE, w=FAKE, pos=FAKE, out=FAKE):
+        return L.mlra_rope_key(ctypes.byref(desc), x, w, pos, out, None)
+
+    for kw in (dict(x=None), dict(w=None), dict(pos=None), dict(out=None)):
+        assert call(**kw) == mlra.ERR_INVALID_ARG, kw
+    assert call(w=ctypes.c_void_p(0x1008)) == mlra.ERR_INVALID_ARG  # W^KR not 16-byte aligned
+    assert call(desc=_desc(d_model=0)) == mlra.ERR_INVALID_ARG
+    assert call(desc=_desc(d_model=64, d_r=4, d_c=64 + 8)) != mlra.OK  # row or d_r % 8 rejected
+    assert call(desc=_desc(d_model=64, rope_base=float("nan"))) == mlra.ERR_INVALID_ARG
+    assert call(desc=_desc(d_model=64, rope_base=float("inf"))) == mlra.ERR_INVALID_ARG
+    # no RoPE key: nothing to do, nothing dereferenced
+    assert call(desc=_desc(d_model=64, d_r=0), x=None, w=None, pos=None, out=None) == mlra.OK
+
+
+def test_project_query_validation():
+    L = mlra.lib()
+    d = _desc(d_model=64, d_cq=32)
+
+    def call(desc=d, x=FAKE, wdq=FAKE, wuq=FAKE, wqr=FAKE, pos=FAKE, cq=FAKE, qc=FAKE, qr=FAKE):
+        return L.mlra_project_query(ctypes.byref(desc), x, wdq, wuq, wqr, pos, cq, qc, qr, None)
+
+    assert call(desc=_desc(d_model=64, d_cq=0)) == mlra.ERR_INVALID_ARG
+    assert call(desc=_desc(d_model=64, d_cq=-8)) == mlra.ERR_INVALID_ARG
+    assert call(desc=_desc(d_model=0, d_cq=32)) == mlra.ERR_INVALID_ARG
+    assert call(desc=_desc(d_model=64, d_cq=36)) == mlra.ERR_UNSUPPORTED  # d_cq % 8
+    assert call(desc=_desc(d_model=64, d_cq=32, d_h=12)) == mlra.ERR_UNSUPPORTED  # d_h % 8
+    for k in ("x", "wdq", "wuq", "wqr", "pos", "cq", "qc", "qr"):
+        assert call(**{k: None}) == mlra.ERR_INVALID_ARG, k
+    for k in ("wdq", "wuq", "wqr"):
+        assert call(**{k: ctypes.c_void_p(0x1004)}) == mlra.ERR_INVALID_ARG, k

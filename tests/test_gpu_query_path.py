@@ -1,0 +1,151 @@
+"""Parity of the steps on either side of the attention with the oracle: the
+RoPE key of the new token and the query path (c^Q, q^C, RoPE'd q^R), through
+the C ABI, and the whole step chained on the device: project the query,
+rotate and append the new token, decode, combine.
+
+Outputs are rounded once from an fp32 accumulation, so the bf16 bar is
+elementwise: |gpu - oracle| <= 2^-8 |oracle| + 1e-3 RMS(oracle) (one bf16
+rounding is at most 2^-9 relative; the RMS term covers fp32 accumulation
+over d_model and d_cq terms). fp32: 1e-5 of max(|oracle|, RMS).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import compressed_kv_cache_mlra_amd as mlra
+import oracle
+import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _check(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), what
+    r = _gpu.rms(ref)
+    if dtype == "f32":
+        err = float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), r)))
+        assert err <= 1e-5, f"{what}: max rel err {err:.3e}"
+    else:
+        excess = np.abs(gpu - ref) - (2.0 ** -8 * np.abs(ref) + 1e-3 * r)
+        assert float(excess.max()) <= 0, f"{what}: bound exceeded by {float(excess.max()):.3e}"
+    return float(np.max(np.abs(gpu - ref))) / r
+
+
+QP_SHAPES = {
+    # several 32-column chunks, 8-sequence groups with a ragged last group
+    "bf16-mlra4": dict(batch=11, n_heads=16, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16",
+                       d_model=1100, d_cq=192),
+    # x and c^Q staged in LDS in more than one 1024-wide chunk, partial last chunk
+    "bf16-wide": dict(batch=3, n_heads=4, d_h=64, d_c=128, n_blocks=1, d_r=32, dtype="bf16",
+                      d_model=2500, d_cq=1064),
+    "f32": dict(batch=9, n_heads=8, d_h=32, d_c=128, n_blocks=2, d_r=16, dtype="f32",
+                d_model=300, d_cq=40),
+    "fp8-cache": dict(batch=5, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
+                      cache_scale=0.125, d_model=512, d_cq=256, rope_base=500.0),
+}
+
+
+def _problem(name, lens=(0, 1, 63, 64, 8191)):
+    kw = dict(QP_SHAPES[name])
+    B = kw.pop("batch")
+    lens = [lens[i % len(lens)] + 7 * i for i in range(B)]
+    s = synth.Shape(batch=B, **kw)
+    inp = synth.make_inputs(s, ("list_append", lens), 4300 + len(name))
+    return s, inp
+
+
+@pytest.mark.parametrize("name", list(QP_SHAPES))
+def test_rope_key(name):
+    _say(f"case: rope_key {name}")
+    t = _gpu.torch()
+    s, inp = _problem(name)
+    prob = _gpu.GpuProblem(inp)
+    desc = prob.desc
+    kr = t.empty((s.batch, s.d_r), dtype=mlra._elem_dtype(desc), device="cuda")
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+    t.cuda.synchronize()
+    got = _bits_to_f64(_gpu.from_dev_bits(kr), s.arrays_dtype)
+    err = _check(got, oracle.rope_key(inp), s.arrays_dtype, "k^R")
+    _say(f"  k^R max err/rms {err:.2e}")
+
+
+@pytest.mark.parametrize("name", list(QP_SHAPES))
+def test_project_query(name):
+    _say(f"case: project_query {name}")
+    t = _gpu.torch()
+    s, inp = _problem(name)
+    prob = _gpu.GpuProblem(inp)
+    desc = prob.desc
+    et = mlra._elem_dtype(desc)
+    cq = t.empty((s.batch, s.d_cq), dtype=t.float32, device="cuda")
+    qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
+    qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
+    mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
+    t.cuda.synchronize()
+    ref_c, ref_r = oracle.project_query(inp)
+    e1 = _check(_bits_to_f64(_gpu.from_dev_bits(qc), s.arrays_dtype), ref_c, s.arrays_dtype, "q^C")
+    e2 = _check(_bits_to_f64(_gpu.from_dev_bits(qr), s.arrays_dtype), ref_r, s.arrays_dtype, "q^R")
+    _say(f"  q^C {e1:.2e}  q^R {e2:.2e}")
+
+
+def test_whole_step_chained_on_device():
+    """project_query -> rope_key -> append_latent -> decode -> combine with
+    every intermediate left on the device, against the oracle run on the
+    oracle's own q^C, q^R and k^R (rounded to bf16 as the device stores them)."""
+    _say("case: chained step")
+    t = _gpu.torch()
+    s, inp = _problem("bf16-mlra4", lens=(5, 200, 64, 1000))
+    prob = _gpu.GpuProblem(inp)
+    desc = prob.desc
+    et = mlra._elem_dtype(desc)
+    cq = t.empty((s.batch, s.d_cq), dtype=t.float32, device="cuda")
+    qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
+    qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
+    kr = t.empty((s.batch, s.d_r), dtype=et, device="cuda")
+    mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+    mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr,
+                       None)
+    mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
+                prob.w_uk, prob.ws)
+    mlra.combine(desc, prob.ws, prob.w_uv, prob.out, prob.lse)
+    t.cuda.synchronize()
+    out = prob.out.cpu().numpy().astype(np.float64)
+
+    # the oracle's own chain: its q^C, q^R, k^R rounded to bf16 like the cache
+    # and the queries the device keeps, its own append, then its decode
+    ref_c, ref_r = oracle.project_query(inp)
+    inp.q_c = synth.f32_to_bf16_bits(ref_c.astype(np.float32))
+    inp.q_r = synth.f32_to_bf16_bits(ref_r.astype(np.float32))
+    inp.kr_new = synth.f32_to_bf16_bits(oracle.rope_key(inp).astype(np.float32))
+    pool_ref = inp.pool.copy()
+    oracle.append(inp, pool_ref)
+    inp.pool = pool_ref
+    pairs = [(b, i) for b in range(s.batch) for i in range(s.n_heads)]
+    ref, _ = oracle.decode_unabsorbed(inp, pairs)
+    g = np.stack([out[b, i] for b, i in pairs])
+    # Bar: this batch mixes 6-token and 1000-token contexts, so the few-token
+    # softmaxes give outputs well above the batch RMS, and the attention's
+    # bf16 rounding of q~ and P (the MFMA operands) shows at their scale: a
+    # numpy emulation of exactly those two roundings on these inputs gives
+    # 2.17e-2 of the RMS (q~ alone 1.98e-2), so the bar here is 2.5e-2.
+    assert np.all(np.isfinite(g))
+    err = float(np.max(np.abs(g - ref))) / _gpu.rms(ref)
+    assert err <= 2.5e-2, f"chained out: max err / rms = {err:.3e}"
+    _say(f"  chained out max err/rms {err:.2e}")
