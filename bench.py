@@ -2,7 +2,8 @@
 
 A step is one pass of the whole decode path over one batch: query absorption,
 split-K latent attention over the paged cache, log-sum-exp combine with the
-value up-projection (plus the latent append for the ragged workload). Inputs are
+value up-projection (plus the latent append for the ragged workload, and the
+query path and RoPE key before it for the whole-layer workload). Inputs are
 seeded synthetic data with the workload's shapes, resident in HBM before timing.
 Several independent cache pools are rotated so the 256 MB Infinity Cache cannot
 serve the cache stream.
@@ -38,7 +39,7 @@ METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8
 KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
 # rocprofv3 counter summaries of the attention kernel, per workload
 PROFILE_TAGS = {2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
-                5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k"}
+                5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k", 7: "mlra4_b32_ctx8k_layer"}
 
 
 def _counters_file(workload: int) -> str:
@@ -52,7 +53,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -137,32 +138,52 @@ def main():
     seq_lens, q_c, q_r = dev(inp.seq_lens), dev(inp.q_c), dev(inp.q_r)
     w_uk, w_uv = dev(inp.w_uk), dev(inp.w_uv)
     append = inp.x is not None
+    qpath = append and s.d_cq > 0
     if append:
-        positions, x, w_dkv, kr_new = dev(inp.positions), dev(inp.x), dev(inp.w_dkv), dev(inp.kr_new)
+        positions, x, kr_new = dev(inp.positions), dev(inp.x), dev(inp.kr_new)
+        # one copy of the step's weights per pool instance, rotated with it, so
+        # that they stream from HBM as a different layer's weights would
+        w_dkv = [dev(inp.w_dkv) for _ in pools]
+    qp_bytes = 0.0
+    if qpath:
+        qpw = [tuple(dev(a) for a in (inp.w_dq, inp.w_uq, inp.w_qr, inp.w_kr)) for _ in pools]
+        et = torch.bfloat16 if s.dtype != "f32" else torch.float32
+        c_q = torch.empty((s.batch, s.d_cq), dtype=torch.float32, device="cuda")
+        q_c = torch.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
+        q_r = torch.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
+        kr_new = torch.empty((s.batch, s.d_r), dtype=et, device="cuda")
+        qp_bytes = float(sum(a.numel() * a.element_size() for a in qpw[0]))
     desc = mlra.make_desc(batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
                           d_r=s.d_r, max_pages_per_seq=inp.max_pages_per_seq,
                           num_pages=pools_np[0].shape[0], dtype=s.dtype, page_size=s.page_size,
-                          blocks_per_head=s.blocks_per_head, d_model=s.d_model, cache_scale=s.cache_scale)
+                          blocks_per_head=s.blocks_per_head, d_model=s.d_model, cache_scale=s.cache_scale,
+                          d_cq=s.d_cq, rope_base=s.rope_base)
     ws = mlra.alloc_workspace(desc, inp.max_seq_len)
     out = torch.empty((s.batch, s.n_heads, s.d_h), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     setup_s = time.time() - t0
 
-    def step(i, ev=None):
-        pool = pools[i % len(pools)]
-        if ev is not None:
-            ev[0].record(stream)
+    def launch(i, cs, mark=lambda k: None):
+        """One step on pool instance i % pools, enqueued on cs; mark(k) is
+        called at the kernel boundaries 0 (start) .. 4 (end)."""
+        p = i % len(pools)
+        mark(0)
+        if qpath:
+            w_dq, w_uq, w_qr, w_kr = qpw[p]
+            mlra.project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, cs)
+            mlra.rope_key(desc, x, w_kr, positions, kr_new, cs)
+            mark(1)
         if append:
-            mlra.append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, None, stream)
-        mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        mlra.attend(desc, pool, page_table, ws, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        mlra.combine(desc, ws, w_uv, out, None, stream)
-        if ev is not None:
-            ev[3].record(stream)
+            mlra.append_latent(desc, pools[p], page_table, positions, x, w_dkv[p], kr_new, None, cs)
+        mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
+        mark(2)
+        mlra.attend(desc, pools[p], page_table, ws, cs)
+        mark(3)
+        mlra.combine(desc, ws, w_uv, out, None, cs)
+        mark(4)
+
+    def step(i, ev=None):
+        launch(i, stream, (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None))
 
     for i in range(args.warmup):
         step(i)
@@ -182,21 +203,20 @@ def main():
 
     # Timed region 2: the same K steps with HIP events around every launch on the
     # launch stream, for the per-kernel durations and the attention roofline.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    attend_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ev_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    qp_ms = [e[0].elapsed_time(e[1]) for e in evs] if qpath else [0.0]
+    pre_ms = [e[1 if qpath else 0].elapsed_time(e[2]) for e in evs]
+    attend_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    comb_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    step_ev_ms = [e[0].elapsed_time(e[4]) for e in evs]
 
     graph_ms_per_step, read_gbps = None, None
     if not args.no_extras:
-        graph_ms_per_step, read_gbps = _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk,
-                                               w_uv, ws, desc, out, stream, append,
-                                               (positions, x, w_dkv, kr_new) if append else None,
+        graph_ms_per_step, read_gbps = _extras(args, torch, mlra, launch, len(pools), stream,
                                                _cache_bytes(inp, s))
 
     n_tokens = int(np.sum(inp.seq_lens.astype(np.int64)))
@@ -238,7 +258,8 @@ def main():
                       "attend_p50": round(1e3 * float(np.percentile(attend_ms, 50)), 2),
                       "attend_p10": round(1e3 * float(np.percentile(attend_ms, 10)), 2),
                       "attend_p90": round(1e3 * float(np.percentile(attend_ms, 90)), 2),
-                      "combine": round(1e3 * float(np.mean(comb_ms)), 2)},
+                      "combine": round(1e3 * float(np.mean(comb_ms)), 2),
+                      "query_path": round(1e3 * float(np.mean(qp_ms)), 2) if qpath else None},
         "roofline": {
             "kernel": "attend_mfma_kernel",
             "bound": "hbm",
@@ -254,6 +275,12 @@ def main():
         },
         "setup_s": round(setup_s, 1),
     }
+    if qpath:
+        # project_query + rope_key: the four weight matrices are their bytes
+        qms = float(np.mean(qp_ms))
+        result["query_path"] = {"weight_bytes": qp_bytes, "us": round(1e3 * qms, 2),
+                                "gbps": round(qp_bytes / (qms * 1e-3) / 1e9, 1),
+                                "frac_of_hbm_peak": round(qp_bytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
@@ -267,22 +294,16 @@ def _cache_bytes(inp, s):
     return float(np.sum(inp.seq_lens.astype(np.int64))) * s.row_bytes
 
 
-def _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk, w_uv, ws, desc, out, stream,
-            append, app, cache_bytes):
+def _extras(args, torch, mlra, launch, n_pools, stream, cache_bytes):
     """(1) The same K steps replayed from HIP graphs, one graph per pool
     instance; (2) a plain streaming read of as many bytes as the attention's
     algorithmic cache bytes, with the attention's loads and launch shape,
     rotated over as many buffers as there are pool instances."""
     graphs = []
-    for p in range(len(pools)):
+    for p in range(n_pools):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream()
-            if append:
-                mlra.append_latent(desc, pools[p], page_table, *app, None, cs)
-            mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
-            mlra.attend(desc, pools[p], page_table, ws, cs)
-            mlra.combine(desc, ws, w_uv, out, None, cs)
+            launch(p, torch.cuda.current_stream())
         graphs.append(g)
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
@@ -297,7 +318,7 @@ def _extras(args, torch, mlra, pools, page_table, seq_lens, q_c, q_r, w_uk, w_uv
     del graphs
 
     rbytes = int(cache_bytes) // 16 * 16
-    rbufs = [torch.empty(rbytes, dtype=torch.uint8, device="cuda") for _ in pools]
+    rbufs = [torch.empty(rbytes, dtype=torch.uint8, device="cuda") for _ in range(n_pools)]
     sink = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
     for i in range(args.warmup):
         mlra.stream_read(rbufs[i % len(rbufs)], sink, stream)

@@ -108,6 +108,13 @@ WORKLOADS = {
             shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
                         cache_scale=1.25),
             lengths=("fixed", 8192)),
+    # the whole layer step around the attention (next-step list): workload 2's
+    # cache and heads plus the query path and the RoPE'd append of the new token
+    7: dict(name="MLRA-4 step with query path + RoPE append, bf16, B=32 h=64 d_h=128 d_c=512(4x128) d_r=64 "
+                 "ctx=8191+1 d_model=4096 d_cq=1536",
+            shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16",
+                        d_model=4096, d_cq=1536),
+            lengths=("uniform_append", 8191, 8191)),
 }
 
 

@@ -149,3 +149,46 @@ def test_whole_step_chained_on_device():
     err = float(np.max(np.abs(g - ref))) / _gpu.rms(ref)
     assert err <= 2.5e-2, f"chained out: max err / rms = {err:.3e}"
     _say(f"  chained out max err/rms {err:.2e}")
+
+
+def test_full_size_layer_workload():
+    """The whole-layer workload at its full size, as the benchmark launches
+    it: k^R, q^C and q^R against the oracle (every element), then the decode
+    on the device's own queries for sampled (sequence, head) pairs."""
+    _say("case: whole-layer workload, full size")
+    t = _gpu.torch()
+    inp = synth.workload_inputs(7)
+    s = inp.shape
+    prob = _gpu.GpuProblem(inp)
+    desc = prob.desc
+    et = mlra._elem_dtype(desc)
+    cq = t.empty((s.batch, s.d_cq), dtype=t.float32, device="cuda")
+    qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
+    qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
+    kr = t.empty((s.batch, s.d_r), dtype=et, device="cuda")
+    mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+    mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr, None)
+    mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
+                prob.w_uk, prob.ws)
+    mlra.combine(desc, prob.ws, prob.w_uv, prob.out, prob.lse)
+    t.cuda.synchronize()
+    kr_b = _gpu.from_dev_bits(kr)
+    qc_b, qr_b = _gpu.from_dev_bits(qc), _gpu.from_dev_bits(qr)
+    _check(_bits_to_f64(kr_b, "bf16"), oracle.rope_key(inp), "bf16", "k^R")
+    ref_c, ref_r = oracle.project_query(inp)
+    _check(_bits_to_f64(qc_b, "bf16"), ref_c, "bf16", "q^C")
+    _check(_bits_to_f64(qr_b, "bf16"), ref_r, "bf16", "q^R")
+    # decode on the device's own q^C, q^R and k^R: the oracle's append and
+    # attention on exactly those inputs
+    inp.q_c, inp.q_r, inp.kr_new = qc_b, qr_b, kr_b
+    pool_ref = inp.pool.copy()
+    oracle.append(inp, pool_ref)
+    inp.pool = pool_ref
+    out = prob.out.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(7)
+    pairs = [(int(b), int(i)) for b, i in zip(rng.integers(0, s.batch, 24), rng.integers(0, s.n_heads, 24))]
+    ref, _ = oracle.decode_unabsorbed(inp, pairs)
+    err = _gpu.check_outputs(np.stack([out[b, i] for b, i in pairs]), ref, "bf16")
+    _say(f"  full-size layer step: out max err/rms {err:.2e}")
