@@ -170,8 +170,8 @@ def main():
         mark(0)
         if qpath:
             w_dq, w_uq, w_qr, w_kr = qpw[p]
-            mlra.project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, cs)
-            mlra.rope_key(desc, x, w_kr, positions, kr_new, cs)
+            mlra.project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, ws, cs)
+            mlra.rope_key(desc, x, w_kr, positions, kr_new, ws, cs)
             mark(1)
         if append:
             mlra.append_latent(desc, pools[p], page_table, positions, x, w_dkv[p], kr_new, None, cs)

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmlra.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MlraError(RuntimeError):
@@ -80,8 +80,8 @@ def lib() -> ctypes.CDLL:
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
         L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
-        L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp]
-        L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp]
+        L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp, ctypes.c_size_t, vp]
+        L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
                   "mlra_combine", "mlra_read_flags", "mlra_stream_read", "mlra_rope_key",
                   "mlra_project_query"):
@@ -193,7 +193,7 @@ def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=Non
         _stream(stream)), "append_latent")
 
 
-def rope_key(desc, x, w_kr, positions, kr_out, stream=None):
+def rope_key(desc, x, w_kr, positions, kr_out, workspace, stream=None):
     """kr_out[b] = RoPE(x[b] W^KR, positions[b]) (feeds append_latent's kr_new)."""
     B = desc.batch
     _check(lib().mlra_rope_key(
@@ -202,10 +202,11 @@ def rope_key(desc, x, w_kr, positions, kr_out, stream=None):
         _ptr(w_kr, desc, name="w_kr", numel=desc.d_model * desc.d_r),
         _ptr(positions, kind="int32", name="positions", numel=B),
         _ptr(kr_out, desc, name="kr_out", numel=B * desc.d_r),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
         _stream(stream)), "rope_key")
 
 
-def project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, stream=None):
+def project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, workspace, stream=None):
     """c_q = x W^DQ (fp32), q_c[:, i] = c_q W^UQ[i], q_r[:, i] = RoPE(c_q W^QR[i])."""
     B, H, DQ = desc.batch, desc.n_heads, desc.d_cq
     no_r = desc.d_r == 0
@@ -219,6 +220,7 @@ def project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, stream=No
         _ptr(c_q, kind="f32", name="c_q", numel=B * DQ),
         _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
         _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=no_r),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
         _stream(stream)), "project_query")
 
 

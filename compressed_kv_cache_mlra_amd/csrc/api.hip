@@ -31,7 +31,7 @@ struct Plan {
   int groups;
   int units;
   int64_t slots;
-  size_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po, total;
+  size_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po, off_proj, total;
   bool q_bf16;
 };
 
@@ -72,9 +72,24 @@ int make_plan(const mlra_desc* d, Plan* p) {
   off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk);
   p->off_po = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk * s.w);
+  p->off_proj = off;  // split-K partials of the projections (rope key, query path)
+  off = align_up(off + proj_scratch_bytes(d));
   p->total = off;
   return MLRA_OK;
 }
+
+}  // namespace
+
+int proj_workspace_region(const mlra_desc* d, size_t* offset, size_t* total) {
+  Plan p;
+  const int st = make_plan(d, &p);
+  if (st != MLRA_OK) return st;
+  *offset = p.off_proj;
+  *total = p.total;
+  return MLRA_OK;
+}
+
+namespace {
 
 // FP8 caches: the value one code unit stands for (1 for other caches).
 float cache_scale_of(const mlra_desc* d) {
@@ -134,7 +149,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 3; }
+int mlra_abi_version(void) { return 4; }
 
 const char* mlra_status_string(int status) {
   switch (status) {

@@ -104,6 +104,35 @@ struct ProjArgs {
   float rope_base;
 };
 
+// One product of a projection launch on the MFMA path (bf16 weights):
+// y[b][m][n] = sum_k x[b][k] W_m[k][n], W_m stored [K][N], optional RoPE.
+struct ProjJob {
+  const void* x;
+  int64_t x_bstride;  // elements between sequences of x (a multiple of 8)
+  int32_t x_f32;      // x is fp32 (split into two bf16 operands), else bf16
+  const uint16_t* w;
+  int64_t w_mstride;
+  void* y;
+  int64_t y_bstride, y_mstride;
+  int32_t y_f32;
+  int32_t K, N;  // multiples of 8
+  int32_t rope;
+  int32_t n_mats;  // matrices W_m (heads) sharing the job
+  int32_t tiles;   // column tiles of N (set by the launcher)
+  int32_t ksplit;  // K slices (set by the launcher); > 1: fp32 partials go to `part`
+  int32_t kper;    // 32-row k-steps per slice (set by the launcher)
+  int32_t wgs;     // workgroups: tiles x sequence groups x matrices x slices (set by the launcher)
+  float* part;     // [ksplit][n_mats][B][N] fp32 partial sums (ksplit > 1)
+};
+struct ProjBatch {
+  ProjJob job[2];
+  int32_t n_jobs;
+  int32_t B;
+  int32_t mgroups;  // groups of 32 sequences
+  const int32_t* positions;
+  float rope_base;
+};
+
 // ------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {

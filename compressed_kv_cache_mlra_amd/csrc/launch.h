@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/mlra.h"
 #include "common.h"
 
 namespace mlra {
@@ -35,5 +36,18 @@ hipError_t launch_append(const AppendArgs& a, int dtype, hipStream_t stream);
 
 // n_mats matrices W_m share one launch (the heads of a per-head projection).
 hipError_t launch_proj(const ProjArgs& a, int n_mats, hipStream_t stream);
+
+// MFMA projection launch: every job's workgroups in one grid. cpl (2 or 4)
+// is the columns each lane loads per weight row; tiles are 16 cpl wide.
+// Products whose column tiles give too few workgroups are split along K;
+// their fp32 partial sums go to `scratch` (bytes from proj_scratch_bytes for
+// the same jobs) and a second kernel sums them in a fixed order and applies
+// the epilogue.
+size_t proj_mfma_scratch_bytes(ProjBatch b, int cpl);
+hipError_t launch_proj_mfma(ProjBatch& b, int cpl, void* scratch, hipStream_t stream);
+// Workspace bytes the projection entry points need for this descriptor, and
+// where that region starts in the workspace (after the decode's regions).
+size_t proj_scratch_bytes(const mlra_desc* d);
+int proj_workspace_region(const mlra_desc* d, size_t* offset, size_t* total);
 
 }  // namespace mlra

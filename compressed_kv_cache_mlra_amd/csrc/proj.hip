@@ -12,6 +12,9 @@
 // k-lanes are summed in LDS, fp32 throughout, one rounding at the end.
 #include <string.h>
 
+#include <algorithm>
+#include <initializer_list>
+
 #include "../../include/mlra.h"
 #include "common.h"
 #include "launch.h"
@@ -141,11 +144,343 @@ __global__ __launch_bounds__(kPThreads) void proj_kernel(ProjArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------- MFMA path
+// At decode batch sizes the products are skinny GEMMs ([B x K] x [K x N] with
+// B of a few dozen) whose weights stream from HBM once; in fp32 VALU the
+// multiply-adds alone would outlast the weight reads, so they go to
+// v_mfma_f32_16x16x32_bf16 with the sequences as MFMA rows (A = x) and the
+// weight columns as MFMA columns (B = W).
+//
+// The B operand wants 8 consecutive k of one column per lane, while W is
+// stored [K][N] (columns contiguous). Each lane therefore loads CPL
+// consecutive columns of 8 consecutive rows (8 small row loads; the 16 lanes
+// of a row group cover 16 CPL contiguous columns) and transposes the 8 x CPL
+// block in registers with v_perm_b32 into CPL operands. Operand e of lane c
+// holds column CPL c + e, so MFMA tile e's output column c is weight column
+// CPL c + e; the epilogue undoes that permutation.
+//
+// Workgroup: 8 waves split the K rows (k-steps of 32 rows, wave-interleaved,
+// 2 or 4 k-steps of loads in flight per wave), 32 sequences (two MFMA row tiles),
+// one tile of 16 CPL columns; the 8 partial accumulators are summed in LDS in
+// a fixed order, then RoPE (pairs 2i, 2i+1, fp64 angles) and the store.
+// An fp32 x (the compressed query) is split into bf16 hi + lo parts, two
+// MFMAs each, which keeps about 16 significant bits of it.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMW = 8;   // waves per workgroup
+constexpr int kMT = 2;   // 16-sequence MFMA row tiles per workgroup
+
+__device__ __forceinline__ floatx4_t mfma_bf16(u32x4_t a, u32x4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // inputs here are finite
+}
+
+// hi + lo bf16 split of 8 fp32 values: hi = RNE(v), lo = RNE(v - hi).
+__device__ __forceinline__ void split8(const u32x4_t& f0, const u32x4_t& f1, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float a = __uint_as_float(u < 2 ? f0[2 * u] : f1[2 * u - 4]);
+    const float b = __uint_as_float(u < 2 ? f0[2 * u + 1] : f1[2 * u - 3]);
+    const uint32_t ha = bf16_rne_bits(a), hb = bf16_rne_bits(b);
+    hi[u] = ha | (hb << 16);
+    const uint32_t la = bf16_rne_bits(a - __uint_as_float(ha << 16));
+    const uint32_t lb = bf16_rne_bits(b - __uint_as_float(hb << 16));
+    lo[u] = la | (lb << 16);
+  }
+}
+
+template <int CPL>
+struct RowBits;
+template <>
+struct RowBits<4> {
+  typedef uint32_t v_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(1))) const v_t g_t;
+};
+template <>
+struct RowBits<2> {
+  typedef uint32_t v_t;
+  typedef __attribute__((address_space(1))) const uint32_t g_t;
+};
+
+typedef __attribute__((address_space(1))) const u32x4_t gq_t;
+
+// Output pair (n, n + 1) of sequence m and matrix mat: RoPE (pair index n / 2,
+// angle pos base^(-n / N) in fp64) if the job asks for it, then one rounding.
+__device__ __forceinline__ void proj_store(const ProjJob& jb, const ProjBatch& a, int mat, int m, int n, float v0,
+                                           float v1) {
+  if (jb.rope) {
+    const double ang = static_cast<double>(a.positions[m]) *
+                       pow(static_cast<double>(a.rope_base), -2.0 * (n >> 1) / jb.N);
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float cs = static_cast<float>(cd), sn = static_cast<float>(sd);
+    const float r0 = v0 * cs - v1 * sn, r1 = v0 * sn + v1 * cs;
+    v0 = r0;
+    v1 = r1;
+  }
+  const int64_t o = static_cast<int64_t>(m) * jb.y_bstride + static_cast<int64_t>(mat) * jb.y_mstride + n;
+  if (jb.y_f32) {
+    float* y = static_cast<float*>(jb.y) + o;
+    y[0] = v0;
+    y[1] = v1;
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(jb.y) + o) =
+        static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+  }
+}
+
+constexpr int proj_kmd(int cpl) { return cpl == 4 ? 2 : 4; }  // k-steps of loads in flight per wave
+
+template <int CPL, bool XF>
+__global__ __launch_bounds__(kMW * 64) void proj_mfma_kernel(ProjBatch a) {
+  constexpr int TC = 16 * CPL;  // tile columns
+  constexpr int NR = kMT * CPL * 4;
+  constexpr int kMD = proj_kmd(CPL);  // register budget
+  typedef typename RowBits<CPL>::v_t v_t;
+  typedef typename RowBits<CPL>::g_t g_t;
+  __shared__ float red[kMW][NR][64];
+  __shared__ float fin[kMT * 16][TC + 1];
+
+  int id = blockIdx.x;
+  const bool second = a.n_jobs > 1 && id >= a.job[0].wgs;
+  if (second) id -= a.job[0].wgs;
+  const ProjJob& jb = second ? a.job[1] : a.job[0];
+  const int K = jb.K, N = jb.N, B = a.B;
+  const int tile = id % jb.tiles;
+  int rest = id / jb.tiles;
+  const int slice = rest % jb.ksplit;
+  rest /= jb.ksplit;
+  const int mg = rest % a.mgroups;
+  const int mat = rest / a.mgroups;
+  const int n0 = tile * TC, m0 = mg * (16 * kMT);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const bool col_ok = n0 + CPL * c < N;
+  // Every load is issued unconditionally from a clamped, valid address and
+  // out-of-range operands are zeroed when used: a load whose destination is
+  // zeroed on another path makes the compiler wait for all loads in flight.
+  const uint16_t* wp = jb.w + static_cast<int64_t>(mat) * jb.w_mstride + (col_ok ? n0 + CPL * c : 0);
+  const int k_lo = slice * jb.kper;                        // this slice's k-steps
+  const int k_hi = min((K + 31) / 32, k_lo + jb.kper);
+  int64_t xrow[kMT];
+  bool m_ok[kMT];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) {
+    const int m = m0 + 16 * t + c;
+    m_ok[t] = m < B;
+    xrow[t] = static_cast<int64_t>(m_ok[t] ? m : B - 1) * jb.x_bstride;
+  }
+
+  floatx4_t acc[kMT][CPL];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[t][e] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks0 = k_lo + wave; ks0 < k_hi; ks0 += kMW * kMD) {
+    v_t rw[kMD][8];
+    u32x4_t ax[kMD][kMT][XF ? 2 : 1];
+    bool kv[kMD];
+#pragma unroll
+    for (int d = 0; d < kMD; ++d) {
+      const int ks = ks0 + d * kMW;
+      const int kb = 32 * ks + 8 * g;  // this lane's 8 rows
+      kv[d] = ks < k_hi && kb < K;     // K % 8 == 0: an 8-row group is whole or absent
+      const int kc = kv[d] ? kb : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rw[d][j] = *(g_t*)(wp + static_cast<int64_t>(kc + j) * N);
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        if constexpr (XF) {
+          const float* xr = static_cast<const float*>(jb.x) + xrow[t] + kc;
+          ax[d][t][0] = *(gq_t*)(xr);
+          ax[d][t][1] = *(gq_t*)(xr + 4);
+        } else {
+          ax[d][t][0] = *(gq_t*)(static_cast<const uint16_t*>(jb.x) + xrow[t] + kc);
+        }
+      }
+    }
+    // keep every load of the chunk ahead of its first use (the scheduler
+    // would otherwise interleave them with the MFMAs, one k-step in flight)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < kMD; ++d) {
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      u32x4_t ahi[kMT], alo[kMT];
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        if constexpr (XF) {
+          split8(ax[d][t][0], ax[d][t][1], ahi[t], alo[t]);
+          if (!(kv[d] && m_ok[t])) alo[t] = z;
+        } else {
+          ahi[t] = ax[d][t][0];
+        }
+        if (!(kv[d] && m_ok[t])) ahi[t] = z;
+      }
+      const bool bok = kv[d] && col_ok;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t bv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t r0, r1;
+          if constexpr (CPL == 4) {
+            r0 = rw[d][2 * u][e >> 1];
+            r1 = rw[d][2 * u + 1][e >> 1];
+          } else {
+            r0 = rw[d][2 * u];
+            r1 = rw[d][2 * u + 1];
+          }
+          bv[u] = bok ? __builtin_amdgcn_perm(r1, r0, sel) : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) {
+          acc[t][e] = mfma_bf16(ahi[t], bv, acc[t][e]);
+          if constexpr (XF) acc[t][e] = mfma_bf16(alo[t], bv, acc[t][e]);
+        }
+      }
+    }
+  }
+
+  // sum the waves' accumulators in a fixed order
+#pragma unroll
+  for (int t = 0; t < kMT; ++t)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][(t * CPL + e) * 4 + i][lane] = acc[t][e][i];
+  __syncthreads();
+  for (int q = threadIdx.x; q < NR * 64; q += kMW * 64) {
+    const int r = q >> 6, ln = q & 63;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) v += red[w][r][ln];
+    const int t = r / (CPL * 4), e = (r >> 2) % CPL, i = r & 3;
+    fin[16 * t + 4 * (ln >> 4) + i][CPL * (ln & 15) + e] = v;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < kMT * 16 * (TC / 2); p += kMW * 64) {
+    const int ml = p / (TC / 2), np = p % (TC / 2);
+    const int m = m0 + ml, n = n0 + 2 * np;
+    if (m >= B || n >= N) continue;
+    const float v0 = fin[ml][2 * np], v1 = fin[ml][2 * np + 1];
+    if (jb.ksplit > 1) {
+      float* pp = jb.part + ((static_cast<int64_t>(slice) * jb.n_mats + mat) * B + m) * N + n;
+      pp[0] = v0;
+      pp[1] = v1;
+    } else {
+      proj_store(jb, a, mat, m, n, v0, v1);
+    }
+  }
+}
+
+// Sums the K slices of every output pair in slice order, then the epilogue.
+__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjBatch a) {
+  int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int B = a.B;
+  for (int j = 0; j < a.n_jobs; ++j) {
+    const ProjJob& jb = a.job[j];
+    const int half = jb.N / 2;
+    const int64_t pairs = static_cast<int64_t>(jb.n_mats) * B * half;
+    if (jb.ksplit > 1 && q < pairs) {
+      const int np = static_cast<int>(q % half);
+      const int64_t mm = q / half;
+      const int m = static_cast<int>(mm % B), mat = static_cast<int>(mm / B);
+      const int n = 2 * np;
+      float v0 = 0.f, v1 = 0.f;
+      for (int s = 0; s < jb.ksplit; ++s) {
+        const float* pp = jb.part + ((static_cast<int64_t>(s) * jb.n_mats + mat) * B + m) * jb.N + n;
+        v0 += pp[0];
+        v1 += pp[1];
+      }
+      proj_store(jb, a, mat, m, n, v0, v1);
+      return;
+    }
+    if (jb.ksplit > 1) q -= pairs;
+  }
+}
 }  // namespace
 
 hipError_t launch_proj(const ProjArgs& a, int n_mats, hipStream_t stream) {
   const dim3 grid((a.N + kPCols - 1) / kPCols, (a.B + kPSeq - 1) / kPSeq, n_mats);
   proj_kernel<<<grid, kPThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kTargetWgs = 512;  // two workgroups per compute unit
+
+// Tiles, K slices and workgroups of every job; returns the partial bytes.
+// A job is split along K until the launch has about kTargetWgs workgroups,
+// each wave of a slice then issues its loads in one go; never more slices
+// than k-step groups of one wave pass (8 waves x k-steps in flight).
+size_t plan_proj(ProjBatch& b, int cpl) {
+  b.mgroups = (b.B + 16 * kMT - 1) / (16 * kMT);
+  int64_t base = 0;
+  for (int j = 0; j < b.n_jobs; ++j) {
+    ProjJob& jb = b.job[j];
+    jb.tiles = (jb.N + 16 * cpl - 1) / (16 * cpl);
+    base += static_cast<int64_t>(jb.tiles) * b.mgroups * jb.n_mats;
+  }
+  const int want = static_cast<int>(std::max<int64_t>(1, (kTargetWgs + base - 1) / base));
+  size_t bytes = 0;
+  for (int j = 0; j < b.n_jobs; ++j) {
+    ProjJob& jb = b.job[j];
+    const int ks = (jb.K + 31) / 32;
+    const int pass = kMW * proj_kmd(cpl);
+    const int most = (ks + pass - 1) / pass;
+    int split = std::min(want, most);
+    jb.kper = (ks + split - 1) / split;
+    jb.ksplit = (ks + jb.kper - 1) / jb.kper;  // no empty slice
+    jb.wgs = jb.tiles * b.mgroups * jb.n_mats * jb.ksplit;
+    if (jb.ksplit > 1)
+      bytes += (sizeof(float) * static_cast<size_t>(jb.ksplit) * jb.n_mats * b.B * jb.N + 255) / 256 * 256;
+  }
+  return bytes;
+}
+
+}  // namespace
+
+size_t proj_mfma_scratch_bytes(ProjBatch b, int cpl) { return plan_proj(b, cpl); }
+
+hipError_t launch_proj_mfma(ProjBatch& b, int cpl, void* scratch, hipStream_t stream) {
+  plan_proj(b, cpl);
+  int total = 0;
+  int64_t pairs = 0;
+  char* sp = static_cast<char*>(scratch);
+  for (int j = 0; j < b.n_jobs; ++j) {
+    ProjJob& jb = b.job[j];
+    total += jb.wgs;
+    if (jb.ksplit > 1) {
+      jb.part = reinterpret_cast<float*>(sp);
+      const size_t n = sizeof(float) * static_cast<size_t>(jb.ksplit) * jb.n_mats * b.B * jb.N;
+      sp += (n + 255) / 256 * 256;
+      pairs += static_cast<int64_t>(jb.n_mats) * b.B * (jb.N / 2);
+    }
+  }
+  const bool xf = b.job[0].x_f32 != 0;  // every job of a launch has the same x type
+  if (cpl == 4 && xf)
+    proj_mfma_kernel<4, true><<<total, kMW * 64, 0, stream>>>(b);
+  else if (cpl == 4)
+    proj_mfma_kernel<4, false><<<total, kMW * 64, 0, stream>>>(b);
+  else if (xf)
+    proj_mfma_kernel<2, true><<<total, kMW * 64, 0, stream>>>(b);
+  else
+    proj_mfma_kernel<2, false><<<total, kMW * 64, 0, stream>>>(b);
+  if (pairs > 0) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    proj_reduce_kernel<<<static_cast<unsigned>((pairs + 255) / 256), 256, 0, stream>>>(b);
+  }
   return hipGetLastError();
 }
 
@@ -164,10 +499,108 @@ float rope_base_of(const mlra_desc* d) { return d->rope_base > 0.f ? d->rope_bas
 // Element type of x, the weights and the outputs (bf16 for FP8 caches).
 bool elems_bf16(const mlra_desc* d) { return d->dtype != MLRA_F32; }
 
+// The MFMA path needs bf16 weights, rows of x in whole 16-byte chunks and
+// 16-byte aligned arrays; anything else runs on the fp32 VALU kernel.
+bool mfma_path(const mlra_desc* d, std::initializer_list<const void*> ptrs) {
+  if (!elems_bf16(d) || d->d_model % 8 != 0) return false;
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+mlra::ProjJob job(const void* x, int64_t x_bstride, bool x_f32, const void* w, int64_t w_mstride, void* y,
+                  int64_t y_bstride, int64_t y_mstride, bool y_f32, int K, int N, bool rope, int n_mats) {
+  mlra::ProjJob j;
+  memset(&j, 0, sizeof(j));
+  j.x = x;
+  j.x_bstride = x_bstride;
+  j.x_f32 = x_f32;
+  j.w = static_cast<const uint16_t*>(w);
+  j.w_mstride = w_mstride;
+  j.y = y;
+  j.y_bstride = y_bstride;
+  j.y_mstride = y_mstride;
+  j.y_f32 = y_f32;
+  j.K = K;
+  j.N = N;
+  j.rope = rope;
+  j.n_mats = n_mats;
+  return j;
+}
+
+// The MFMA launches of the two entry points (pointers may be null when sizing).
+mlra::ProjBatch rope_batch(const mlra_desc* d, const void* x, const void* w_kr, const int32_t* pos, void* kr) {
+  mlra::ProjBatch b;
+  memset(&b, 0, sizeof(b));
+  b.job[0] = job(x, d->d_model, false, w_kr, 0, kr, d->d_r, 0, false, d->d_model, d->d_r, true, 1);
+  b.n_jobs = 1;
+  b.B = d->batch;
+  b.positions = pos;
+  b.rope_base = rope_base_of(d);
+  return b;
+}
+
+// c^Q = x W^DQ, kept in fp32
+mlra::ProjBatch query_batch1(const mlra_desc* d, const void* x, const void* w_dq, float* c_q) {
+  mlra::ProjBatch b;
+  memset(&b, 0, sizeof(b));
+  b.job[0] = job(x, d->d_model, false, w_dq, 0, c_q, d->d_cq, 0, true, d->d_model, d->d_cq, false, 1);
+  b.n_jobs = 1;
+  b.B = d->batch;
+  return b;
+}
+
+// q^C_i = c^Q W^UQ_i and q^R_i = RoPE(c^Q W^QR_i), every head, one launch
+mlra::ProjBatch query_batch2(const mlra_desc* d, const float* c_q, const void* w_uq, const void* w_qr,
+                             const int32_t* pos, void* q_c, void* q_r) {
+  const int H = d->n_heads, DQ = d->d_cq, DH = d->d_h, DR = d->d_r;
+  mlra::ProjBatch b;
+  memset(&b, 0, sizeof(b));
+  b.job[0] = job(c_q, DQ, true, w_uq, static_cast<int64_t>(DQ) * DH, q_c, static_cast<int64_t>(H) * DH, DH, false,
+                 DQ, DH, false, H);
+  b.n_jobs = 1;
+  if (DR > 0) {
+    b.job[1] = job(c_q, DQ, true, w_qr, static_cast<int64_t>(DQ) * DR, q_r, static_cast<int64_t>(H) * DR, DR, false,
+                   DQ, DR, true, H);
+    b.n_jobs = 2;
+  }
+  b.B = d->batch;
+  b.positions = pos;
+  b.rope_base = rope_base_of(d);
+  return b;
+}
+
+constexpr int kCplRope = 2, kCplQuery1 = 2, kCplQuery2 = 4;
+
+// Checks the workspace and returns the start of the projection region.
+int proj_scratch(const mlra_desc* d, void* workspace, size_t ws_bytes, void** scratch) {
+  size_t off = 0, total = 0;
+  const int st = mlra::proj_workspace_region(d, &off, &total);
+  if (st != MLRA_OK) return st;
+  if (!workspace) return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < total) return MLRA_ERR_WORKSPACE;
+  *scratch = static_cast<char*>(workspace) + off;
+  return MLRA_OK;
+}
+
 }  // namespace
 
+size_t mlra::proj_scratch_bytes(const mlra_desc* d) {
+  if (!elems_bf16(d) || d->d_model < 1 || d->d_model % 8 != 0) return 0;  // VALU path: no scratch
+  size_t need = 0;
+  if (d->d_r > 0 && d->d_r % 8 == 0)
+    need = std::max(need, proj_mfma_scratch_bytes(rope_batch(d, nullptr, nullptr, nullptr, nullptr), kCplRope));
+  if (d->d_cq > 0 && d->d_cq % 8 == 0 && d->d_h % 8 == 0 && d->d_r % 8 == 0) {
+    need = std::max(need, proj_mfma_scratch_bytes(query_batch1(d, nullptr, nullptr, nullptr), kCplQuery1));
+    need = std::max(need, proj_mfma_scratch_bytes(
+                              query_batch2(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), kCplQuery2));
+  }
+  return need;
+}
+
 extern "C" int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
-                             const int32_t* positions, void* kr_out, void* stream) {
+                             const int32_t* positions, void* kr_out, void* workspace, size_t ws_bytes,
+                             void* stream) {
   using namespace mlra;
   int st = check_desc(desc, nullptr);
   if (st != MLRA_OK) return st;
@@ -175,6 +608,14 @@ extern "C" int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w
   if (desc->d_r == 0) return MLRA_OK;
   if (desc->d_r % 8 != 0) return MLRA_ERR_UNSUPPORTED;
   if (!x || !w_kr || !positions || !kr_out || !aligned16(w_kr)) return MLRA_ERR_INVALID_ARG;
+  void* scratch = nullptr;
+  st = proj_scratch(desc, workspace, ws_bytes, &scratch);
+  if (st != MLRA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma_path(desc, {x, kr_out})) {
+    ProjBatch b = rope_batch(desc, x, w_kr, positions, kr_out);
+    return proj_status(launch_proj_mfma(b, kCplRope, scratch, s));
+  }
   const bool bf = elems_bf16(desc);
   ProjArgs a;
   memset(&a, 0, sizeof(a));
@@ -192,12 +633,13 @@ extern "C" int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w
   a.positions = positions;
   a.rope = 1;
   a.rope_base = rope_base_of(desc);
-  return proj_status(launch_proj(a, 1, static_cast<hipStream_t>(stream)));
+  return proj_status(launch_proj(a, 1, s));
 }
 
 extern "C" int mlra_project_query(const mlra_desc* desc, const void* x, const void* w_dq,
                                   const void* w_uq, const void* w_qr, const int32_t* positions,
-                                  float* c_q, void* q_c, void* q_r, void* stream) {
+                                  float* c_q, void* q_c, void* q_r, void* workspace, size_t ws_bytes,
+                                  void* stream) {
   using namespace mlra;
   int st = check_desc(desc, nullptr);
   if (st != MLRA_OK) return st;
@@ -206,8 +648,18 @@ extern "C" int mlra_project_query(const mlra_desc* desc, const void* x, const vo
   if (!x || !w_dq || !w_uq || !c_q || !q_c) return MLRA_ERR_INVALID_ARG;
   if (desc->d_r > 0 && (!w_qr || !q_r || !positions)) return MLRA_ERR_INVALID_ARG;
   if (!aligned16(w_dq) || !aligned16(w_uq) || (desc->d_r > 0 && !aligned16(w_qr))) return MLRA_ERR_INVALID_ARG;
+  void* scratch = nullptr;
+  st = proj_scratch(desc, workspace, ws_bytes, &scratch);
+  if (st != MLRA_OK) return st;
   const bool bf = elems_bf16(desc);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma_path(desc, {x, c_q, q_c, q_r})) {
+    ProjBatch b1 = query_batch1(desc, x, w_dq, c_q);
+    st = proj_status(launch_proj_mfma(b1, kCplQuery1, scratch, s));
+    if (st != MLRA_OK) return st;
+    ProjBatch b2 = query_batch2(desc, c_q, w_uq, w_qr, positions, q_c, q_r);
+    return proj_status(launch_proj_mfma(b2, kCplQuery2, scratch, s));
+  }
   ProjArgs a;
   memset(&a, 0, sizeof(a));
   // c^Q = x W^DQ, kept in fp32

@@ -102,7 +102,9 @@ typedef struct {
   float rope_base;           /* RoPE frequency base (<= 0 selects 10000) */
 } mlra_desc;
 
-/* Bytes of device workspace mlra_decode / mlra_combine need for this shape.
+/* Bytes of device workspace mlra_decode / mlra_combine need for this shape,
+ * plus, with d_model (and d_cq) set, the split-K scratch of mlra_rope_key and
+ * mlra_project_query: one workspace serves every entry point of a layer.
  * Depends on the shape and on the number of compute units of the current
  * device, not on the sequence lengths. Returns 0 for an invalid descriptor.
  * max_seq_len: upper bound of the lengths the workspace will be used with
@@ -175,9 +177,16 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
  *   x: [batch][d_model]; w_kr: 16-byte aligned; positions: int32 [batch]
  *   (device); kr_out: [batch][d_r], ready to be passed to mlra_append_latent
  *   as kr_new. Element type: desc->dtype (bf16 for MLRA_FP8_E4M3).
+ *   workspace: at least mlra_workspace_bytes(desc, .) bytes (the decode's
+ *   workspace; calls sharing it must be ordered on one stream), else
+ *   MLRA_ERR_WORKSPACE; its contents before the call do not matter.
+ * With bf16 weights, d_model % 8 == 0 and 16-byte aligned x and kr_out the
+ * products run on MFMA (bf16 x and W, fp32 accumulation); otherwise on an fp32
+ * VALU kernel. Results are deterministic (fixed summation order).
  * d_r == 0 does nothing; d_r % 8 != 0 is MLRA_ERR_UNSUPPORTED. */
 int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
-                  const int32_t* positions, void* kr_out, void* stream);
+                  const int32_t* positions, void* kr_out, void* workspace, size_t ws_bytes,
+                  void* stream);
 
 /* The query path (lesty.tech section 4: the query is compressed and split like
  * the key; MLA's parameter count on the "Multi-Head Low-Rank Attention" paper
@@ -190,10 +199,14 @@ int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
  * and q_r are rounded once to the element type (desc->dtype, bf16 for
  * MLRA_FP8_E4M3) and feed mlra_absorb_query / mlra_decode directly.
  * Weights 16-byte aligned; d_cq, d_h and d_r multiples of 8 (else
- * MLRA_ERR_UNSUPPORTED); with d_r == 0, w_qr, q_r and positions may be NULL. */
+ * MLRA_ERR_UNSUPPORTED); with d_r == 0, w_qr, q_r and positions may be NULL.
+ * workspace as for mlra_rope_key. On the MFMA path (same conditions as
+ * mlra_rope_key, with c_q, q_c and q_r 16-byte aligned) c_q enters the second
+ * and third products as two bf16 parts (c_q = hi + lo, about 16 significant
+ * bits). */
 int mlra_project_query(const mlra_desc* desc, const void* x, const void* w_dq, const void* w_uq,
                        const void* w_qr, const int32_t* positions, float* c_q, void* q_c,
-                       void* q_r, void* stream);
+                       void* q_r, void* workspace, size_t ws_bytes, void* stream);
 
 /* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host memory),
  * after the work already enqueued on `stream` (synchronises it). The flags are

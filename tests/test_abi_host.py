@@ -188,8 +188,9 @@ def test_rope_key_validation():
     L = mlra.lib()
     d = _desc(d_model=64)
 
-    def call(desc=d, x=FAKE, w=FAKE, pos=FAKE, out=FAKE):
-        return L.mlra_rope_key(ctypes.byref(desc), x, w, pos, out, None)
+    def call(desc=d, x=FAKE, w=FAKE, pos=FAKE, out=FAKE, ws=FAKE, ws_bytes=16):
+        # ws_bytes far too small: a call that passes every other check stops there
+        return L.mlra_rope_key(ctypes.byref(desc), x, w, pos, out, ws, ctypes.c_size_t(ws_bytes), None)
 
     for kw in (dict(x=None), dict(w=None), dict(pos=None), dict(out=None)):
         assert call(**kw) == mlra.ERR_INVALID_ARG, kw
@@ -200,14 +201,18 @@ def test_rope_key_validation():
     assert call(desc=_desc(d_model=64, rope_base=float("inf"))) == mlra.ERR_INVALID_ARG
     # no RoPE key: nothing to do, nothing dereferenced
     assert call(desc=_desc(d_model=64, d_r=0), x=None, w=None, pos=None, out=None) == mlra.OK
+    assert call() == mlra.ERR_WORKSPACE
+    assert call(ws=None) == mlra.ERR_INVALID_ARG
 
 
 def test_project_query_validation():
     L = mlra.lib()
     d = _desc(d_model=64, d_cq=32)
 
-    def call(desc=d, x=FAKE, wdq=FAKE, wuq=FAKE, wqr=FAKE, pos=FAKE, cq=FAKE, qc=FAKE, qr=FAKE):
-        return L.mlra_project_query(ctypes.byref(desc), x, wdq, wuq, wqr, pos, cq, qc, qr, None)
+    def call(desc=d, x=FAKE, wdq=FAKE, wuq=FAKE, wqr=FAKE, pos=FAKE, cq=FAKE, qc=FAKE, qr=FAKE, ws=FAKE,
+             ws_bytes=16):
+        return L.mlra_project_query(ctypes.byref(desc), x, wdq, wuq, wqr, pos, cq, qc, qr, ws,
+                                    ctypes.c_size_t(ws_bytes), None)
 
     assert call(desc=_desc(d_model=64, d_cq=0)) == mlra.ERR_INVALID_ARG
     assert call(desc=_desc(d_model=64, d_cq=-8)) == mlra.ERR_INVALID_ARG
@@ -218,3 +223,18 @@ def test_project_query_validation():
         assert call(**{k: None}) == mlra.ERR_INVALID_ARG, k
     for k in ("wdq", "wuq", "wqr"):
         assert call(**{k: ctypes.c_void_p(0x1004)}) == mlra.ERR_INVALID_ARG, k
+    assert call() == mlra.ERR_WORKSPACE
+    assert call(ws=None) == mlra.ERR_INVALID_ARG
+
+
+def test_projection_scratch_is_part_of_the_workspace():
+    """bf16 layers with a query path need split-K scratch beyond the decode's
+    regions; fp32 layers (VALU path) need none."""
+    L = mlra.lib()
+    kw = dict(dtype="bf16", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64)
+    plain = _desc(**kw)
+    layer = _desc(d_model=4096, d_cq=1536, **kw)
+    assert L.mlra_workspace_bytes(ctypes.byref(layer), 10) > L.mlra_workspace_bytes(ctypes.byref(plain), 10)
+    f32 = _desc(d_model=4096, d_cq=64)
+    f32_plain = _desc()
+    assert L.mlra_workspace_bytes(ctypes.byref(f32), 10) == L.mlra_workspace_bytes(ctypes.byref(f32_plain), 10)

@@ -46,11 +46,15 @@ def _check(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
 
 
 QP_SHAPES = {
-    # several 32-column chunks, 8-sequence groups with a ragged last group
+    # MFMA path: several column tiles, 11 sequences (a partial row tile)
     "bf16-mlra4": dict(batch=11, n_heads=16, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16",
-                       d_model=1100, d_cq=192),
-    # x and c^Q staged in LDS in more than one 1024-wide chunk, partial last chunk
-    "bf16-wide": dict(batch=3, n_heads=4, d_h=64, d_c=128, n_blocks=1, d_r=32, dtype="bf16",
+                       d_model=1096, d_cq=192),
+    # MFMA path: two groups of 32 sequences; d_model and d_cq end in a partial
+    # 32-row k-step (2504 = 78 x 32 + 8, 1064 = 33 x 32 + 8)
+    "bf16-wide": dict(batch=37, n_heads=4, d_h=64, d_c=128, n_blocks=1, d_r=32, dtype="bf16",
+                      d_model=2504, d_cq=1064),
+    # d_model not a multiple of 8: the fp32 VALU kernel, x staged in several chunks
+    "bf16-valu": dict(batch=3, n_heads=4, d_h=64, d_c=128, n_blocks=1, d_r=32, dtype="bf16",
                       d_model=2500, d_cq=1064),
     "f32": dict(batch=9, n_heads=8, d_h=32, d_c=128, n_blocks=2, d_r=16, dtype="f32",
                 d_model=300, d_cq=40),
@@ -76,7 +80,7 @@ def test_rope_key(name):
     prob = _gpu.GpuProblem(inp)
     desc = prob.desc
     kr = t.empty((s.batch, s.d_r), dtype=mlra._elem_dtype(desc), device="cuda")
-    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr, prob.ws)
     t.cuda.synchronize()
     got = _bits_to_f64(_gpu.from_dev_bits(kr), s.arrays_dtype)
     err = _check(got, oracle.rope_key(inp), s.arrays_dtype, "k^R")
@@ -95,7 +99,7 @@ def test_project_query(name):
     qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
     qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
     mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
-                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr, prob.ws)
     t.cuda.synchronize()
     ref_c, ref_r = oracle.project_query(inp)
     e1 = _check(_bits_to_f64(_gpu.from_dev_bits(qc), s.arrays_dtype), ref_c, s.arrays_dtype, "q^C")
@@ -118,8 +122,8 @@ def test_whole_step_chained_on_device():
     qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
     kr = t.empty((s.batch, s.d_r), dtype=et, device="cuda")
     mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
-                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
-    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr, prob.ws)
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr, prob.ws)
     mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr,
                        None)
     mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
@@ -140,14 +144,9 @@ def test_whole_step_chained_on_device():
     pairs = [(b, i) for b in range(s.batch) for i in range(s.n_heads)]
     ref, _ = oracle.decode_unabsorbed(inp, pairs)
     g = np.stack([out[b, i] for b, i in pairs])
-    # Bar: this batch mixes 6-token and 1000-token contexts, so the few-token
-    # softmaxes give outputs well above the batch RMS, and the attention's
-    # bf16 rounding of q~ and P (the MFMA operands) shows at their scale: a
-    # numpy emulation of exactly those two roundings on these inputs gives
-    # 2.17e-2 of the RMS (q~ alone 1.98e-2), so the bar here is 2.5e-2.
-    assert np.all(np.isfinite(g))
-    err = float(np.max(np.abs(g - ref))) / _gpu.rms(ref)
-    assert err <= 2.5e-2, f"chained out: max err / rms = {err:.3e}"
+    # a numpy emulation of the attention's bf16 roundings of q~ and P on these
+    # inputs (short and long contexts mixed) reaches 1.73e-2 of the RMS
+    err = _gpu.check_outputs(g, ref, "bf16")
     _say(f"  chained out max err/rms {err:.2e}")
 
 
@@ -167,8 +166,8 @@ def test_full_size_layer_workload():
     qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
     kr = t.empty((s.batch, s.d_r), dtype=et, device="cuda")
     mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
-                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr)
-    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr)
+                       _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr, prob.ws)
+    mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr, prob.ws)
     mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr, None)
     mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
                 prob.w_uk, prob.ws)
