@@ -94,9 +94,10 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
         const int mid = (lo + hi + 1) >> 1;
         if (cum_sh[mid] <= x0) lo = mid; else hi = mid - 1;
       }
+      const bool nxt = lo + 1 < a.batch;
       int4* dst = reinterpret_cast<int4*>(udesc + static_cast<int64_t>(u) * kUnitDescInts);
       dst[0] = make_int4(x0, x1, lo, cum_sh[lo]);
-      dst[1] = make_int4(cum_sh[lo + 1], len_sh[lo], 0, 0);
+      dst[1] = make_int4(cum_sh[lo + 1], len_sh[lo], nxt ? cum_sh[lo + 2] : NT, nxt ? len_sh[lo + 1] : 0);
     }
     if (tid == 0) {
       WsHeader* h = reinterpret_cast<WsHeader*>(a.ws);

@@ -203,6 +203,13 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     }
     return phys;
   };
+  auto checked = [&](int32_t phys) __attribute__((always_inline)) -> int32_t {
+    if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) {
+      phys = 0;
+      bad_page = 1;
+    }
+    return phys;
+  };
   // Physical page of the j-th page of tile x (x at the load cursor).
   auto page_of = [&](int32_t x, int j) __attribute__((always_inline)) -> int32_t {
     if (use_tab) return __builtin_amdgcn_readfirstlane(ptab[(x - x0) * npt + j]);
@@ -321,19 +328,35 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     return min(C::TT, sc_n - (x - sc_start) * C::TT);
   };
 
-  // ---- prologue: tile x0 into LDS buffer 0, tile x0+1 in flight
+  // ---- prologue: with the descriptor in hand, tile x0 (its page looked up
+  // with a scalar load), the query and the page ids of the rest of the unit
+  // are requested together; tile x0+1 follows once x0 is in LDS.
   u32x4_t ring[C::NL];
   load_tile(x0, ring);
-  store_tile(ring, lds, store_valid(x0));
-  if (x0 + 1 < x1) load_tile(x0 + 1, ring);
 
-  // ---- page ids of the rest of the unit, gathered into LDS while tile x0+1
-  // is in flight
-  {
+  const int32_t nx_end = cload(ud + 6), nx_n = cload(ud + 7);  // the sequence after lo
+  const int32_t ntab = (x1 - x0) * npt;
+  if (ntab <= C::PT_CAP && x1 <= nx_end) {
+    // every tile of the unit lies in sequence lo or lo + 1
+    for (int i = tid; i < ntab; i += C::NTHREADS) {
+      const int32_t x = x0 + i / npt;
+      const int j = i % npt;
+      const bool first = x < pb_end;
+      const int b = first ? lo : lo + 1;
+      const int32_t start = first ? pb_start : pb_end;
+      const int32_t n = first ? pb_n : nx_n;
+      const int32_t npg = (n + P - 1) >> a.log2_page;
+      const int32_t pg0 = (((x - start) * C::TT) >> a.log2_page) + j;
+      const int32_t pg = pg0 < npg ? pg0 : npg - 1;
+      ptab[i] = checked(a.page_table ? a.page_table[static_cast<int64_t>(b) * a.max_pages + pg]
+                                     : b * a.max_pages + pg);
+    }
+    __syncthreads();
+    use_tab = true;
+  } else {
     const int win = min(C::SEQ_WIN, a.batch - lo);
     if (tid < win) seq_end[tid] = cum[lo + 1 + tid];
     __syncthreads();
-    const int32_t ntab = (x1 - x0) * npt;
     if (ntab <= C::PT_CAP && x1 <= seq_end[win - 1]) {
       const int32_t lo_start = cb_start;
       for (int i = tid; i < ntab; i += C::NTHREADS) {
@@ -347,18 +370,15 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         const int32_t npg = (n + P - 1) >> a.log2_page;
         const int32_t pg0 = (((x - start) * C::TT) >> a.log2_page) + j;
         const int32_t pg = pg0 < npg ? pg0 : npg - 1;
-        int32_t phys = a.page_table ? a.page_table[static_cast<int64_t>(b) * a.max_pages + pg]
-                                    : b * a.max_pages + pg;
-        if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) {
-          phys = 0;
-          bad_page = 1;
-        }
-        ptab[i] = phys;
+        ptab[i] = checked(a.page_table ? a.page_table[static_cast<int64_t>(b) * a.max_pages + pg]
+                                       : b * a.max_pages + pg);
       }
       use_tab = true;
     }
     __syncthreads();
   }
+  store_tile(ring, lds, store_valid(x0));
+  if (x0 + 1 < x1) load_tile(x0 + 1, ring);
 
   auto step = [&](int32_t x) __attribute__((always_inline)) {
     const int t = x - x0;

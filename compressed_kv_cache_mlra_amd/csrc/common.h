@@ -31,8 +31,9 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 constexpr uint32_t kWsMagic = 0x4d4c5241u;  // "MLRA"
 constexpr uint32_t kFlagBadPage = 1u;       // same value as MLRA_FLAG_BAD_PAGE
 constexpr int kMaxBatch = 4096;             // sequences per call (the plan keeps them in LDS)
-// Per-unit descriptor written by the plan: {first tile, end tile, sequence of
-// the first tile, that sequence's first tile, its end tile, its length, 0, 0}.
+// Per-unit plan descriptor (ints): 0 first tile x0, 1 end tile x1, 2 sequence
+// lo owning x0, 3 cum[lo], 4 cum[lo + 1], 5 length of lo, 6 cum[lo + 2] (the
+// tile count when lo is the last sequence), 7 length of lo + 1 (0 if none).
 constexpr int kUnitDescInts = 8;
 
 // Everything a decode kernel needs, passed by value.
