@@ -56,6 +56,9 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
   if (tid == kAbsorbThreads - 1) cum_sh[a.batch] = part_sh[kAbsorbThreads - 1];
   __syncthreads();
   const int32_t NT = cum_sh[a.batch];
+  // With fewer tiles than launched units only the first NT units get work (one
+  // tile each), so every unit a sequence's range meets holds a partial.
+  const int32_t UE = NT < a.units ? (NT > 0 ? NT : 1) : a.units;
 
   {  // in global memory for the attention and the combine
     int32_t* cum = reinterpret_cast<int32_t*>(a.ws + a.off_cum);
@@ -69,8 +72,8 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
       const int32_t xa = cum_sh[b], xb = cum_sh[b + 1];
       int32_t u0 = 0, u1 = -1;
       if (xa < xb) {
-        u0 = unit_of_tile(xa, NT, a.units);
-        u1 = unit_of_tile(xb - 1, NT, a.units);
+        u0 = unit_of_tile(xa, NT, UE);
+        u1 = unit_of_tile(xb - 1, NT, UE);
       }
       sunit[2 * b] = u0;
       sunit[2 * b + 1] = u1;
@@ -87,7 +90,7 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
     for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
     int32_t* udesc = reinterpret_cast<int32_t*>(a.ws + a.off_udesc);
     for (int u = tid; u < a.units; u += kAbsorbThreads) {
-      const int32_t x0 = tile_begin(u, NT, a.units), x1 = tile_begin(u + 1, NT, a.units);
+      const int32_t x0 = u < UE ? tile_begin(u, NT, UE) : NT, x1 = u < UE ? tile_begin(u + 1, NT, UE) : NT;
       // sequence owning tile x0: the largest b with cum_sh[b] <= x0
       int lo = 0, hi = a.batch - 1;
       while (lo < hi) {
@@ -104,7 +107,7 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
       h->magic = kWsMagic;
       h->flags = 0;
       h->n_tiles = NT;
-      h->units = a.units;
+      h->units = UE;  // units that may hold partials
       h->tile_tokens = a.tile_tokens;
       h->groups = a.groups;
       h->batch = a.batch;

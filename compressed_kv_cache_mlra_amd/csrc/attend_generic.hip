@@ -30,11 +30,12 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(DecodeArgs a) {
   const int QW = a.w + a.d_r;
 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
-  const int32_t NT = hdr->n_tiles;
+  const int32_t NT = hdr->n_tiles, units = hdr->units;
   const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
   const int32_t* nlen = reinterpret_cast<const int32_t*>(a.ws + a.off_nlen);
-  const int32_t x0 = tile_begin(unit, NT, a.units);
-  const int32_t x1 = tile_begin(unit + 1, NT, a.units);
+  if (unit >= units) return;
+  const int32_t x0 = tile_begin(unit, NT, units);
+  const int32_t x1 = tile_begin(unit + 1, NT, units);
   if (x0 >= x1) return;
   int lo = 0, hi = a.batch - 1;
   while (lo < hi) {
