@@ -42,7 +42,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false>
+template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false, bool CF_ = false>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -53,6 +53,10 @@ struct Cfg {
   static constexpr int OCC = OCC_;  // workgroups resident per compute unit
   static constexpr int ROW = NBR * W + DR;
   static constexpr bool F8 = F8_;     // cache rows hold E4M3FN latent codes, then bf16 k^R
+  // Step order: CF computes tile x before storing tile x+1 (so the first tile
+  // is computed without waiting for the second); otherwise x+1 is stored and
+  // x+2 requested before tile x is computed. Chosen per shape by measurement.
+  static constexpr bool CF = CF_;
   static constexpr int ROWB = ROW * 2;  // bytes of a row in LDS (bf16 throughout)
   static constexpr int CPR = ROW / 8;   // 16-byte LDS chunks per row
   static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROWB;  // bytes of a row in HBM
@@ -394,10 +398,16 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     }
     const int valid = min(C::TT, cb_n - (x - cb_start) * C::TT);
     // Tile x is in its buffer for every wave and every wave is done with
-    // tile x-1: tile x+1 goes registers -> the other buffer, tile x+2 is
-    // requested into the registers.
+    // tile x-1: tile x+1 goes registers -> the other buffer (before or after
+    // tile x is computed), tile x+2 is requested into the registers.
     lds_barrier();
-    if constexpr (C::OCC == 1) {
+    if constexpr (C::CF) {
+      if (need_q) {
+        // a new sequence starts inside this unit: its query before any MFMA
+        load_q(cb);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+    } else if constexpr (C::OCC == 1) {
       // One workgroup per compute unit: nothing else hides this workgroup's
       // memory waits, so tile x+2 stays in flight while tile x is computed.
       // The query of a new sequence is loaded and waited for first, so no
@@ -539,6 +549,14 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       m_run = -INFINITY;
       l_run = 0.f;
     }
+    if constexpr (C::CF) {
+      // tile x+1 has been in flight since the previous step; its buffer was
+      // left by every wave at this step's barrier, the next barrier publishes it
+      if (x + 1 < x1) {
+        store_tile(ring, lds + ((t + 1) & 1) * C::TILE_BYTES, store_valid(x + 1));
+        if (x + 2 < x1) load_tile(x + 2, ring);
+      }
+    }
   };
 
   for (int32_t x = x0; x < x1; ++x) step(x);
@@ -556,30 +574,34 @@ struct Entry {
   hipError_t (*fn)(const DecodeArgs&, hipStream_t);
 };
 
-template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false>
+template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8>;
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF>;
   return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? 1 : 0, C::NTHREADS, 2 * C::TILE_BYTES},
                &run_variant<C>};
 }
 
 // Shapes with a tuned MFMA kernel. Key: (w, d_r, blocks per row, 16-head tiles per block).
+// Step order (last flag, compute-first): measured per shape on one box, same
+// binary A/B: compute-first is 4-7% faster for the TP-share, MLRA-2 and FP8
+// MLRA-4 kernels and 6-7% slower for bf16 MLRA-4 and MLA; the FP8 TP-share and
+// MLRA-2 kernels follow their bf16 counterparts.
 const Entry kVariants[] = {
     entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
     entry<512, 64, 1, 4, 1, 32, 1>(),   // MLA: one 512 latent, 64 heads
     // one MLRA-4 block (a TP rank's share), <= 16 heads: one-wave workgroups,
     // four per compute unit, each streaming its own 32-token tiles (measured
     // 1.8x faster than four waves sharing 128-token tiles at one per unit)
-    entry<128, 64, 1, 1, 1, 32, 4>(),
-    entry<256, 64, 2, 2, 1, 32, 2>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
+    entry<128, 64, 1, 1, 1, 32, 4, false, true>(),
+    entry<256, 64, 2, 2, 1, 32, 2, false, true>(),   // MLRA-2: 2 x 256 latent, <= 32 heads per block
     entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
     entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
     entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
     // FP8 (E4M3FN) caches of the same shapes and tunings
-    entry<128, 64, 4, 1, 1, 32, 2, true>(),
+    entry<128, 64, 4, 1, 1, 32, 2, true, true>(),
     entry<512, 64, 1, 4, 1, 32, 1, true>(),
-    entry<128, 64, 1, 1, 1, 32, 4, true>(),
-    entry<256, 64, 2, 2, 1, 32, 2, true>(),
+    entry<128, 64, 1, 1, 1, 32, 4, true, true>(),
+    entry<256, 64, 2, 2, 1, 32, 2, true, true>(),
 };
 
 }  // namespace
