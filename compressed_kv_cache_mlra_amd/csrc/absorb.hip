@@ -82,12 +82,18 @@ __device__ void plan_block(const DecodeArgs& a, const int32_t* seq_lens) {
     const int hk_all = a.n_heads * a.k;
     float* pm = reinterpret_cast<float*>(a.ws + a.off_pm) + static_cast<int64_t>(a.empty_slot) * hk_all;
     float* pl = reinterpret_cast<float*>(a.ws + a.off_pl) + static_cast<int64_t>(a.empty_slot) * hk_all;
-    float* po = reinterpret_cast<float*>(a.ws + a.off_po) + static_cast<int64_t>(a.empty_slot) * hk_all * a.w;
+    const int64_t po0 = static_cast<int64_t>(a.empty_slot) * hk_all * a.w;  // first element of the empty slot
     for (int i = tid; i < hk_all; i += kAbsorbThreads) {
       pm[i] = -INFINITY;
       pl[i] = 0.f;
     }
-    for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
+    if (a.po_f16) {
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.ws + a.off_po) + po0;
+      for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0;
+    } else {
+      float* po = reinterpret_cast<float*>(a.ws + a.off_po) + po0;
+      for (int i = tid; i < hk_all * a.w; i += kAbsorbThreads) po[i] = 0.f;
+    }
     int32_t* udesc = reinterpret_cast<int32_t*>(a.ws + a.off_udesc);
     for (int u = tid; u < a.units; u += kAbsorbThreads) {
       const int32_t x0 = u < UE ? tile_begin(u, NT, UE) : NT, x1 = u < UE ? tile_begin(u + 1, NT, UE) : NT;

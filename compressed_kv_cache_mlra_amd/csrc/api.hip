@@ -71,7 +71,9 @@ int make_plan(const mlra_desc* d, Plan* p) {
   p->off_pl = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk);
   p->off_po = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk * s.w);
+  // weighted latent sums: fp16 on the MFMA path (rows scaled into (-1, 1) by a
+  // power of two folded into m and l), fp32 on the generic path
+  off = align_up(off + (p->variant ? 2 : 4) * static_cast<size_t>(p->slots) * s.hk * s.w);
   p->off_proj = off;  // split-K partials of the projections (rope key, query path)
   off = align_up(off + proj_scratch_bytes(d));
   p->total = off;
@@ -111,6 +113,7 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.off_pm = static_cast<int64_t>(p.off_pm);
   a.off_pl = static_cast<int64_t>(p.off_pl);
   a.off_po = static_cast<int64_t>(p.off_po);
+  a.po_f16 = p.variant ? 1 : 0;
   a.batch = d->batch;
   a.n_heads = d->n_heads;
   a.d_h = d->d_h;
@@ -231,6 +234,7 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   c.off_pm = static_cast<int64_t>(p.off_pm);
   c.off_pl = static_cast<int64_t>(p.off_pl);
   c.off_po = static_cast<int64_t>(p.off_po);
+  c.po_f16 = p.variant ? 1 : 0;
   c.batch = desc->batch;
   c.n_heads = desc->n_heads;
   c.d_h = desc->d_h;

@@ -118,6 +118,12 @@ __device__ __forceinline__ floatx4_t mfma32(bf16x8_t a, bf16x8_t b, floatx4_t c)
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // v_cvt_pk_bf16_f32 (RNE)
   return __builtin_bit_cast(uint32_t, v);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 
   float* pm = reinterpret_cast<float*>(a.ws + a.off_pm);
   float* pl = reinterpret_cast<float*>(a.ws + a.off_pl);
-  float* po = reinterpret_cast<float*>(a.ws + a.off_po);
+  uint16_t* po = reinterpret_cast<uint16_t*>(a.ws + a.off_po);  // fp16 weighted latent sums
   const uint16_t* qext = reinterpret_cast<const uint16_t*>(a.ws + a.off_qext);
 
   auto load_q = [&](int b) __attribute__((always_inline)) {
@@ -529,17 +535,36 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // ---- segment end: write this wave's partial and reset.
       const float l_tot = sum_4lanes(l_run);
       const int64_t slot = static_cast<int64_t>(unit + cb) * C::G + tgrp;
+      // The head's row of weighted sums is scaled by 2^-s, s the exponent of
+      // its largest magnitude, and stored as fp16 (values in (-1, 1), 11-bit
+      // precision); m + s and l 2^-s go with it, which leaves every ratio the
+      // combine forms unchanged.
+      float amax = 0.f;
+#pragma unroll
+      for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(O[q][e][i]));
+      amax = max_4lanes(amax);
+      int sexp = 0;
+      if (amax > 0.f) frexpf(amax, &sexp);
+      const float rs = ldexpf(1.f, -sexp);
       if (head_ok) {
-        float* dst = po + (slot * HK + hk) * C::W;
+        // column 128 q + 8 (4 g4 + i) + e holds O[q][e][i]: 8 consecutive
+        // columns per (q, i), one 16-byte store
+        uint16_t* dst = po + (slot * HK + hk) * C::W;
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[128 * q + 8 * (4 * g4 + i) + e] = O[q][e][i];
+          for (int i = 0; i < 4; ++i) {
+            const u32x4_t v = {pack_f16x2(O[q][0][i] * rs, O[q][1][i] * rs), pack_f16x2(O[q][2][i] * rs, O[q][3][i] * rs),
+                               pack_f16x2(O[q][4][i] * rs, O[q][5][i] * rs), pack_f16x2(O[q][6][i] * rs, O[q][7][i] * rs)};
+            *reinterpret_cast<u32x4_t*>(dst + 128 * q + 8 * (4 * g4 + i)) = v;
+          }
         if (g4 == 0) {
-          pm[slot * HK + hk] = m_run;
-          pl[slot * HK + hk] = l_tot;
+          pm[slot * HK + hk] = m_run + static_cast<float>(sexp);
+          pl[slot * HK + hk] = l_tot * rs;
         }
       }
 #pragma unroll

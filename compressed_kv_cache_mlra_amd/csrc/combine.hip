@@ -54,7 +54,7 @@ __device__ __forceinline__ float2 load_pair<float, false>(const float* p, int64_
   return make_float2(p[i], p[i2]);
 }
 
-template <typename TW, bool EVEN>
+template <typename TW, bool EVEN, bool PB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   extern __shared__ float sh[];
   float* ot = sh;                             // [k * w][kBatchGroup]
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int32_t* sunit = reinterpret_cast<const int32_t*>(a.ws + a.off_sunit);
   const float* pm = reinterpret_cast<const float*>(a.ws + a.off_pm);
   const float* pl = reinterpret_cast<const float*>(a.ws + a.off_pl);
-  const float* po = reinterpret_cast<const float*>(a.ws + a.off_po);
+  const char* po = a.ws + a.off_po;
   const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;  // first entry of the empty slot
 
 
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
           const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + s % G) * a.hk + hk : empty_hk + hk;
           ms[u] = pm[idx];
           ls[u] = pl[idx];
-          vs[u] = *reinterpret_cast<const float4*>(po + idx * a.w + c);
+          vs[u] = load_partial4<PB>(po, idx * a.w + c);
         }
         float mb = M;
 #pragma unroll
@@ -268,7 +268,7 @@ __device__ __forceinline__ float sum_lanes_16_32_48(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int W, int KB>
+template <int W, int KB, bool PB>
 __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs a) {
   constexpr int K = W * KB;               // merged latent columns per head
   constexpr int CG = K / 4;               // 4-column groups per sequence
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
   const int32_t* sunit = reinterpret_cast<const int32_t*>(a.ws + a.off_sunit);
   const float* pm = reinterpret_cast<const float*>(a.ws + a.off_pm);
   const float* pl = reinterpret_cast<const float*>(a.ws + a.off_pl);
-  const float* po = reinterpret_cast<const float*>(a.ws + a.off_po);
+  const char* po = a.ws + a.off_po;
   const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;
 
   // ---- merge
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
           const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + sl % G) * a.hk + hk : empty_hk + hk;
           ms[u] = pm[idx];
           ls[u] = pl[idx];
-          vs[u] = *reinterpret_cast<const float4*>(po + idx * W + c);
+          vs[u] = load_partial4<PB>(po, idx * W + c);
         }
         float mb = M;
 #pragma unroll
@@ -436,7 +436,10 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
 template <int W, int KB>
 void launch_fast(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_heads, (a.batch + kFastSeq - 1) / kFastSeq);
-  combine_fast_kernel<W, KB><<<grid, kFastThreads, 0, stream>>>(a);
+  if (a.po_f16)
+    combine_fast_kernel<W, KB, true><<<grid, kFastThreads, 0, stream>>>(a);
+  else
+    combine_fast_kernel<W, KB, false><<<grid, kFastThreads, 0, stream>>>(a);
 }
 
 // Runs the specialised combine when the shape has one; false otherwise.
@@ -463,11 +466,17 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
   const size_t sh = sizeof(float) * (kBatchGroup * a.k * a.w + kThreads * 2 * kBatchGroup);
   const bool even = a.d_h % 2 == 0;
   if (dtype == 1) {
-    if (even) combine_kernel<uint16_t, true><<<grid, kThreads, sh, stream>>>(a);
-    else combine_kernel<uint16_t, false><<<grid, kThreads, sh, stream>>>(a);
+    if (a.po_f16) {
+      if (even) combine_kernel<uint16_t, true, true><<<grid, kThreads, sh, stream>>>(a);
+      else combine_kernel<uint16_t, false, true><<<grid, kThreads, sh, stream>>>(a);
+    } else {
+      if (even) combine_kernel<uint16_t, true, false><<<grid, kThreads, sh, stream>>>(a);
+      else combine_kernel<uint16_t, false, false><<<grid, kThreads, sh, stream>>>(a);
+    }
   } else {
-    if (even) combine_kernel<float, true><<<grid, kThreads, sh, stream>>>(a);
-    else combine_kernel<float, false><<<grid, kThreads, sh, stream>>>(a);
+    // fp32 arrays run the generic attention, which keeps fp32 partials
+    if (even) combine_kernel<float, true, false><<<grid, kThreads, sh, stream>>>(a);
+    else combine_kernel<float, false, false><<<grid, kThreads, sh, stream>>>(a);
   }
   return hipGetLastError();
 }

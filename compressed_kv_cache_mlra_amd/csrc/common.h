@@ -42,6 +42,8 @@ struct DecodeArgs {
   const int32_t* page_table;  // nullptr: identity layout
   char* ws;
   int64_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po;
+  int32_t po_f16;     // weighted latent sums of the partials stored as fp16 rows scaled by a
+                      // power of two folded into m and l (MFMA path), else fp32
   int32_t batch;
   int32_t n_heads;
   int32_t d_h;
@@ -82,6 +84,7 @@ struct CombineArgs {
   float* out;
   float* lse;
   int64_t off_sunit, off_pm, off_pl, off_po;
+  int32_t po_f16;  // as DecodeArgs::po_f16
   int32_t batch, n_heads, d_h, w, k, hk;
   int32_t groups;      // head groups per work unit (partial slots per unit and sequence)
   int32_t empty_slot;  // partial slot that always reads as empty (m = -inf, l = 0, o~ = 0)
@@ -135,6 +138,21 @@ struct ProjBatch {
 };
 
 // ------------------------------------------------------------- device helpers
+
+// Four consecutive weighted-latent values of a partial, fp32 or fp16 storage.
+template <bool PH>
+__device__ __forceinline__ float4 load_partial4(const char* po, int64_t i);
+template <>
+__device__ __forceinline__ float4 load_partial4<false>(const char* po, int64_t i) {
+  return *reinterpret_cast<const float4*>(po + 4 * i);
+}
+template <>
+__device__ __forceinline__ float4 load_partial4<true>(const char* po, int64_t i) {
+  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+  const half4_t v = *reinterpret_cast<const half4_t*>(po + 2 * i);
+  return make_float4(static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                     static_cast<float>(v[3]));
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
