@@ -152,7 +152,8 @@ def main():
         q_c = torch.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
         q_r = torch.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
         kr_new = torch.empty((s.batch, s.d_r), dtype=et, device="cuda")
-        qp_bytes = float(sum(a.numel() * a.element_size() for a in qpw[0]))
+        qp_bytes = float(sum(a.numel() * a.element_size() for a in qpw[0]) +
+                         w_dkv[0].numel() * w_dkv[0].element_size())
     desc = mlra.make_desc(batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
                           d_r=s.d_r, max_pages_per_seq=inp.max_pages_per_seq,
                           num_pages=pools_np[0].shape[0], dtype=s.dtype, page_size=s.page_size,
@@ -169,12 +170,13 @@ def main():
         p = i % len(pools)
         mark(0)
         if qpath:
+            # the token's projections: latent append, RoPE key, query path
             w_dq, w_uq, w_qr, w_kr = qpw[p]
-            mlra.project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, ws, cs)
-            mlra.rope_key(desc, x, w_kr, positions, kr_new, ws, cs)
+            mlra.project_token(desc, x, positions, pools[p], page_table, w_dkv[p], w_kr, kr_new, None, w_dq,
+                               w_uq, w_qr, c_q, q_c, q_r, ws, cs)
             mark(1)
-        if append:
-            mlra.append_latent(desc, pools[p], page_table, positions, x, w_dkv[p], kr_new, None, cs)
+        elif append:
+            mlra.append_latent(desc, pools[p], page_table, positions, x, w_dkv[p], kr_new, None, ws, cs)
         mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
         mark(2)
         mlra.attend(desc, pools[p], page_table, ws, cs)
@@ -259,7 +261,7 @@ def main():
                       "attend_p10": round(1e3 * float(np.percentile(attend_ms, 10)), 2),
                       "attend_p90": round(1e3 * float(np.percentile(attend_ms, 90)), 2),
                       "combine": round(1e3 * float(np.mean(comb_ms)), 2),
-                      "query_path": round(1e3 * float(np.mean(qp_ms)), 2) if qpath else None},
+                      "token_projections": round(1e3 * float(np.mean(qp_ms)), 2) if qpath else None},
         "roofline": {
             "kernel": "attend_mfma_kernel",
             "bound": "hbm",
@@ -276,9 +278,10 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if qpath:
-        # project_query + rope_key: the four weight matrices are their bytes
+        # project_token (latent append, RoPE key, query path): its five weight
+        # matrices are its HBM bytes
         qms = float(np.mean(qp_ms))
-        result["query_path"] = {"weight_bytes": qp_bytes, "us": round(1e3 * qms, 2),
+        result["token_projections"] = {"weight_bytes": qp_bytes, "us": round(1e3 * qms, 2),
                                 "gbps": round(qp_bytes / (qms * 1e-3) / 1e9, 1),
                                 "frac_of_hbm_peak": round(qp_bytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 

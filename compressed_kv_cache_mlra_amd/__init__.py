@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmlra.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class MlraError(RuntimeError):
@@ -73,7 +73,9 @@ def lib() -> ctypes.CDLL:
         L.mlra_status_string.restype = ctypes.c_char_p
         L.mlra_workspace_bytes.argtypes = [dp, ctypes.c_int32]
         L.mlra_workspace_bytes.restype = ctypes.c_size_t
-        L.mlra_append_latent.argtypes = [dp, vp, ip, ip, vp, vp, vp, vp, vp]
+        L.mlra_append_latent.argtypes = [dp, vp, ip, ip, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mlra_project_token.argtypes = [dp, vp, ip, vp, ip, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
         L.mlra_absorb_query.argtypes = [dp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mlra_attend.argtypes = [dp, vp, ip, vp, ctypes.c_size_t, vp]
         L.mlra_decode.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -84,7 +86,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
                   "mlra_combine", "mlra_read_flags", "mlra_stream_read", "mlra_rope_key",
-                  "mlra_project_query"):
+                  "mlra_project_query", "mlra_project_token"):
             getattr(L, f).restype = ctypes.c_int
         if L.mlra_abi_version() != ABI_VERSION:
             raise ImportError("libmlra ABI version mismatch; rebuild the library")
@@ -178,7 +180,7 @@ def _w(desc):
     return desc.d_c // desc.n_blocks
 
 
-def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=None, stream=None):
+def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out, workspace, stream=None):
     B = desc.batch
     _check(lib().mlra_append_latent(
         ctypes.byref(desc),
@@ -188,9 +190,41 @@ def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out=Non
         _ptr(x, desc, name="x", numel=B * desc.d_model),
         _ptr(w_dkv, desc, name="w_dkv", numel=desc.d_model * desc.d_c),
         _ptr(kr_new, desc, name="kr_new", numel=B * desc.d_r, nullable=desc.d_r == 0),
-        (_ptr(c_out, kind="f32", name="c_out", numel=B * desc.d_c, nullable=True) if desc.dtype == FP8_E4M3
-         else _ptr(c_out, desc, name="c_out", numel=B * desc.d_c, nullable=True)),
+        _c_out_ptr(c_out, desc),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
         _stream(stream)), "append_latent")
+
+
+def _c_out_ptr(c_out, desc):
+    """c_out: fp32 for FP8 caches (the latent before encoding), else the element type; optional."""
+    if desc.dtype == FP8_E4M3:
+        return _ptr(c_out, kind="f32", name="c_out", numel=desc.batch * desc.d_c, nullable=True)
+    return _ptr(c_out, desc, name="c_out", numel=desc.batch * desc.d_c, nullable=True)
+
+
+def project_token(desc, x, positions, pool, page_table, w_dkv, w_kr, kr_out, c_out, w_dq, w_uq, w_qr, c_q, q_c,
+                  q_r, workspace, stream=None):
+    """rope_key + append_latent + project_query of the new token in one call."""
+    B, H, DQ = desc.batch, desc.n_heads, desc.d_cq
+    no_q, no_r = DQ == 0, desc.d_r == 0
+    _check(lib().mlra_project_token(
+        ctypes.byref(desc),
+        _ptr(x, desc, name="x", numel=B * desc.d_model),
+        _ptr(positions, kind="int32", name="positions", numel=B),
+        _pool_ptr(pool, desc),
+        _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
+        _ptr(w_dkv, desc, name="w_dkv", numel=desc.d_model * desc.d_c),
+        _ptr(w_kr, desc, name="w_kr", numel=desc.d_model * desc.d_r, nullable=no_r),
+        _ptr(kr_out, desc, name="kr_out", numel=B * desc.d_r, nullable=no_r),
+        _c_out_ptr(c_out, desc),
+        _ptr(w_dq, desc, name="w_dq", numel=desc.d_model * DQ, nullable=no_q),
+        _ptr(w_uq, desc, name="w_uq", numel=H * DQ * desc.d_h, nullable=no_q),
+        _ptr(w_qr, desc, name="w_qr", numel=H * DQ * desc.d_r, nullable=no_q or no_r),
+        _ptr(c_q, kind="f32", name="c_q", numel=B * DQ, nullable=no_q),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h, nullable=no_q),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=no_q or no_r),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _stream(stream)), "project_token")
 
 
 def rope_key(desc, x, w_kr, positions, kr_out, workspace, stream=None):

@@ -152,7 +152,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 4; }
+int mlra_abi_version(void) { return 5; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -251,7 +251,7 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
 
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,
                        const int32_t* positions, const void* x, const void* w_dkv,
-                       const void* kr_new, void* c_out, void* stream) {
+                       const void* kr_new, void* c_out, void* workspace, size_t ws_bytes, void* stream) {
   ShapeInfo s;
   int st = check_desc(desc, &s);
   if (st != MLRA_OK) return st;
@@ -259,6 +259,9 @@ int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_ta
   if (st != MLRA_OK) return st;
   if (!pool || !positions || !x || !w_dkv || (desc->d_r > 0 && !kr_new)) return MLRA_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(w_dkv) % 16 != 0) return MLRA_ERR_INVALID_ARG;  // 16-byte row loads
+  st = append_latent_mfma(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out, workspace, ws_bytes, stream);
+  if (st != kNotEligible) return st;
+  if (!workspace) return MLRA_ERR_INVALID_ARG;  // the same contract on every path
   AppendArgs a;
   memset(&a, 0, sizeof(a));
   a.pool = pool;

@@ -42,22 +42,6 @@ struct Row8<float> {
   __device__ __forceinline__ float get(int j) const { return __uint_as_float(j < 4 ? v0[j] : v1[j - 4]); }
 };
 
-// Nearest OCP E4M3FN code of x, ties to even; magnitudes of 448 and above
-// saturate to 448 and NaN gives 0x7F. Codes in the binade [2^E, 2^(E+1))
-// (E >= -6) are spaced 2^(E-3) and the subnormal spacing 2^-9 continues below
-// 2^-6, so with E' = max(E, -6) the nearest multiple n 2^(E'-3) of |x|
-// (n in 0..16) has code (E' + 6) 8 + n.
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  if (x != x) return 0x7Fu;
-  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a >= 448.f) return sgn | 0x7Eu;
-  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // floor(log2 a); zero -> -127
-  if (e < -6) e = -6;
-  const float n = rintf(a * __uint_as_float(static_cast<uint32_t>(130 - e) << 23));  // a 2^(3-e), exact
-  return sgn | static_cast<uint32_t>((e + 6) * 8 + static_cast<int>(n));
-}
-
 // grid: n_chunks * batch, chunk fastest, so consecutive workgroups (which the
 // dispatcher spreads over the 8 XCDs) cover different column chunks and each
 // XCD's L2 keeps reusing one chunk of W^DKV across the batch.

@@ -121,6 +121,7 @@ struct ProjJob {
   int32_t y_f32;
   int32_t K, N;  // multiples of 8
   int32_t rope;
+  int32_t kind;    // epilogue: kProjStore, kProjLatentRow or kProjRopeRow
   int32_t n_mats;  // matrices W_m (heads) sharing the job
   int32_t tiles;   // column tiles of N (set by the launcher)
   int32_t ksplit;  // K slices (set by the launcher); > 1: fp32 partials go to `part`
@@ -128,16 +129,50 @@ struct ProjJob {
   int32_t wgs;     // workgroups: tiles x sequence groups x matrices x slices (set by the launcher)
   float* part;     // [ksplit][n_mats][B][N] fp32 partial sums (ksplit > 1)
 };
+// Epilogues of a projection job:
+//   kProjStore      y[b][m][n] (fp32 or bf16), optional RoPE;
+//   kProjLatentRow  the latent of token positions[b] into its pool row (bf16,
+//                   or FP8 codes of value x cache_inv) and c_out; with kr_src
+//                   the given RoPE key is copied into the row as well;
+//   kProjRopeRow    RoPE, then the RoPE key into the row and into y (kr_out).
+constexpr int kProjStore = 0, kProjLatentRow = 1, kProjRopeRow = 2;
+constexpr int kProjMaxJobs = 3;
 struct ProjBatch {
-  ProjJob job[2];
+  ProjJob job[kProjMaxJobs];
   int32_t n_jobs;
   int32_t B;
   int32_t mgroups;  // groups of 32 sequences
   const int32_t* positions;
   float rope_base;
+  // pool rows (row epilogues)
+  void* pool;
+  const int32_t* page_table;  // nullptr: identity layout
+  int32_t page_size, max_pages, num_pages;
+  int32_t row_bytes;  // bytes per pool row
+  int32_t d_c, d_r;
+  int32_t fp8;        // FP8 E4M3FN latent codes (else bf16)
+  float cache_inv;    // FP8: fp32 reciprocal of the cache scale
+  void* c_out;        // latent before rounding/encoding: fp32 (FP8) or bf16; may be null
+  const uint16_t* kr_src;  // bf16 RoPE keys [B][d_r] to copy into the rows; may be null
 };
 
 // ------------------------------------------------------------- device helpers
+
+// Nearest OCP E4M3FN code of x, ties to even; magnitudes of 448 and above
+// saturate to 448 and NaN gives 0x7F. Codes in the binade [2^E, 2^(E+1))
+// (E >= -6) are spaced 2^(E-3) and the subnormal spacing 2^-9 continues below
+// 2^-6, so with E' = max(E, -6) the nearest multiple n 2^(E'-3) of |x|
+// (n in 0..16) has code (E' + 6) 8 + n.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  if (x != x) return 0x7Fu;
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a >= 448.f) return sgn | 0x7Eu;
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // floor(log2 a); zero -> -127
+  if (e < -6) e = -6;
+  const float n = rintf(a * __uint_as_float(static_cast<uint32_t>(130 - e) << 23));  // a 2^(3-e), exact
+  return sgn | static_cast<uint32_t>((e + 6) * 8 + static_cast<int>(n));
+}
 
 // Four consecutive weighted-latent values of a partial, fp32 or fp16 storage.
 template <bool PH>

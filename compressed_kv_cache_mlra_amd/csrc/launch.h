@@ -48,6 +48,11 @@ hipError_t launch_proj_mfma(ProjBatch& b, int cpl, void* scratch, hipStream_t st
 // Workspace bytes the projection entry points need for this descriptor, and
 // where that region starts in the workspace (after the decode's regions).
 size_t proj_scratch_bytes(const mlra_desc* d);
+// mlra_append_latent on MFMA; kNotEligible when its inputs need the fp32 kernel.
+constexpr int kNotEligible = 1;
+int append_latent_mfma(const mlra_desc* desc, void* pool, const int32_t* page_table, const int32_t* positions,
+                       const void* x, const void* w_dkv, const void* kr_new, void* c_out, void* workspace,
+                       size_t ws_bytes, void* stream);
 int proj_workspace_region(const mlra_desc* d, size_t* offset, size_t* total);
 
 }  // namespace mlra

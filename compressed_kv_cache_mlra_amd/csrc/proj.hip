@@ -211,10 +211,54 @@ struct RowBits<2> {
 
 typedef __attribute__((address_space(1))) const u32x4_t gq_t;
 
+__device__ __forceinline__ uint32_t bf16_pair(float v0, float v1) {
+  return static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+}
+
+// Byte address of the pool row of token positions[m], or nullptr when the
+// position or its page is out of range (nothing is written then).
+__device__ __forceinline__ uint8_t* pool_row(const ProjBatch& a, int m) {
+  const int32_t pos = a.positions[m];
+  if (pos < 0 || pos >= a.max_pages * a.page_size) return nullptr;
+  const int32_t pidx = pos / a.page_size;
+  const int32_t phys = a.page_table ? a.page_table[static_cast<int64_t>(m) * a.max_pages + pidx]
+                                    : m * a.max_pages + pidx;
+  if (static_cast<uint32_t>(phys) >= static_cast<uint32_t>(a.num_pages)) return nullptr;
+  return static_cast<uint8_t*>(a.pool) +
+         (static_cast<int64_t>(phys) * a.page_size + pos % a.page_size) * a.row_bytes;
+}
+
 // Output pair (n, n + 1) of sequence m and matrix mat: RoPE (pair index n / 2,
-// angle pos base^(-n / N) in fp64) if the job asks for it, then one rounding.
+// angle pos base^(-n / N) in fp64) if the job asks for it, then one rounding,
+// into the job's destination.
 __device__ __forceinline__ void proj_store(const ProjJob& jb, const ProjBatch& a, int mat, int m, int n, float v0,
                                            float v1) {
+  if (jb.kind == kProjLatentRow) {
+    uint8_t* row = pool_row(a, m);
+    if (!row) return;
+    if (a.fp8) {
+      *reinterpret_cast<uint16_t*>(row + n) =
+          static_cast<uint16_t>(e4m3_encode(v0 * a.cache_inv) | (e4m3_encode(v1 * a.cache_inv) << 8));
+      if (a.c_out) {
+        float* c = static_cast<float*>(a.c_out) + static_cast<int64_t>(m) * a.d_c + n;
+        c[0] = v0;
+        c[1] = v1;
+      }
+    } else {
+      const uint32_t pr = bf16_pair(v0, v1);
+      *reinterpret_cast<uint32_t*>(row + 2 * n) = pr;
+      if (a.c_out)
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.c_out) + static_cast<int64_t>(m) * a.d_c + n) = pr;
+    }
+    if (a.kr_src) {
+      // the given RoPE key: pairs n, n + d_c, ... of it
+      uint16_t* rope = reinterpret_cast<uint16_t*>(row + (a.fp8 ? a.d_c : 2 * a.d_c));
+      for (int r = n; r < a.d_r; r += a.d_c)
+        *reinterpret_cast<uint32_t*>(rope + r) =
+            *reinterpret_cast<const uint32_t*>(a.kr_src + static_cast<int64_t>(m) * a.d_r + r);
+    }
+    return;
+  }
   if (jb.rope) {
     const double ang = static_cast<double>(a.positions[m]) *
                        pow(static_cast<double>(a.rope_base), -2.0 * (n >> 1) / jb.N);
@@ -225,14 +269,18 @@ __device__ __forceinline__ void proj_store(const ProjJob& jb, const ProjBatch& a
     v0 = r0;
     v1 = r1;
   }
+  if (jb.kind == kProjRopeRow) {
+    uint8_t* row = pool_row(a, m);
+    if (row) *reinterpret_cast<uint32_t*>(row + (a.fp8 ? a.d_c : 2 * a.d_c) + 2 * n) = bf16_pair(v0, v1);
+  }
+  if (!jb.y) return;
   const int64_t o = static_cast<int64_t>(m) * jb.y_bstride + static_cast<int64_t>(mat) * jb.y_mstride + n;
   if (jb.y_f32) {
     float* y = static_cast<float*>(jb.y) + o;
     y[0] = v0;
     y[1] = v1;
   } else {
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(jb.y) + o) =
-        static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(jb.y) + o) = bf16_pair(v0, v1);
   }
 }
 
@@ -249,9 +297,21 @@ __global__ __launch_bounds__(kMW * 64) void proj_mfma_kernel(ProjBatch a) {
   __shared__ float fin[kMT * 16][TC + 1];
 
   int id = blockIdx.x;
-  const bool second = a.n_jobs > 1 && id >= a.job[0].wgs;
-  if (second) id -= a.job[0].wgs;
-  const ProjJob& jb = second ? a.job[1] : a.job[0];
+  // the job this workgroup belongs to (id becomes the index inside it),
+  // copied with constant indices so the arguments stay out of scratch memory
+  int jsel = 0;
+  if (a.n_jobs > 1 && id >= a.job[0].wgs) {
+    id -= a.job[0].wgs;
+    jsel = 1;
+    if (a.n_jobs > 2 && id >= a.job[1].wgs) {
+      id -= a.job[1].wgs;
+      jsel = 2;
+    }
+  }
+  ProjJob jb;
+  if (jsel == 0) __builtin_memcpy(&jb, &a.job[0], sizeof(ProjJob));
+  else if (jsel == 1) __builtin_memcpy(&jb, &a.job[1], sizeof(ProjJob));
+  else __builtin_memcpy(&jb, &a.job[2], sizeof(ProjJob));
   const int K = jb.K, N = jb.N, B = a.B;
   const int tile = id % jb.tiles;
   int rest = id / jb.tiles;
@@ -386,7 +446,9 @@ __global__ __launch_bounds__(kMW * 64) void proj_mfma_kernel(ProjBatch a) {
 __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjBatch a) {
   int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int B = a.B;
-  for (int j = 0; j < a.n_jobs; ++j) {
+#pragma unroll
+  for (int j = 0; j < kProjMaxJobs; ++j) {
+    if (j >= a.n_jobs) return;
     const ProjJob& jb = a.job[j];
     const int half = jb.N / 2;
     const int64_t pairs = static_cast<int64_t>(jb.n_mats) * B * half;
@@ -570,7 +632,57 @@ mlra::ProjBatch query_batch2(const mlra_desc* d, const float* c_q, const void* w
   return b;
 }
 
-constexpr int kCplRope = 2, kCplQuery1 = 2, kCplQuery2 = 4;
+// The latent append (kProjLatentRow) into the pool rows of positions[b];
+// kr_new (bf16) is copied into the rows' RoPE part.
+void set_pool(mlra::ProjBatch& b, const mlra_desc* d, void* pool, const int32_t* page_table, void* c_out) {
+  b.pool = pool;
+  b.page_table = page_table;
+  b.page_size = d->page_size;
+  b.max_pages = d->max_pages_per_seq;
+  b.num_pages = d->num_pages;
+  b.fp8 = d->dtype == MLRA_FP8_E4M3;
+  b.row_bytes = b.fp8 ? d->d_c + 2 * d->d_r : 2 * (d->d_c + d->d_r);
+  b.d_c = d->d_c;
+  b.d_r = d->d_r;
+  b.cache_inv = 1.0f / (d->cache_scale > 0.f ? d->cache_scale : 1.0f);
+  b.c_out = c_out;
+}
+
+mlra::ProjBatch append_batch(const mlra_desc* d, const void* x, const void* w_dkv, const int32_t* pos, void* pool,
+                             const int32_t* page_table, const void* kr_new, void* c_out) {
+  mlra::ProjBatch b;
+  memset(&b, 0, sizeof(b));
+  b.job[0] = job(x, d->d_model, false, w_dkv, 0, nullptr, 0, 0, false, d->d_model, d->d_c, false, 1);
+  b.job[0].kind = mlra::kProjLatentRow;
+  b.n_jobs = 1;
+  b.B = d->batch;
+  b.positions = pos;
+  set_pool(b, d, pool, page_table, c_out);
+  b.kr_src = static_cast<const uint16_t*>(kr_new);
+  return b;
+}
+
+// Everything the new token's hidden state x feeds, one launch: its latent into
+// the pool row, its RoPE key into the row (and kr_out), and (d_cq > 0) the
+// compressed query c^Q.
+mlra::ProjBatch token_batch(const mlra_desc* d, const void* x, const int32_t* pos, void* pool,
+                            const int32_t* page_table, const void* w_dkv, const void* w_kr, void* kr_out, void* c_out,
+                            const void* w_dq, float* c_q) {
+  mlra::ProjBatch b = append_batch(d, x, w_dkv, pos, pool, page_table, nullptr, c_out);
+  b.rope_base = rope_base_of(d);
+  if (d->d_r > 0) {
+    b.job[b.n_jobs] = job(x, d->d_model, false, w_kr, 0, kr_out, d->d_r, 0, false, d->d_model, d->d_r, true, 1);
+    b.job[b.n_jobs].kind = mlra::kProjRopeRow;
+    ++b.n_jobs;
+  }
+  if (d->d_cq > 0) {
+    b.job[b.n_jobs] = job(x, d->d_model, false, w_dq, 0, c_q, d->d_cq, 0, true, d->d_model, d->d_cq, false, 1);
+    ++b.n_jobs;
+  }
+  return b;
+}
+
+constexpr int kCplRope = 2, kCplQuery1 = 2, kCplQuery2 = 4, kCplToken = 2;
 
 // Checks the workspace and returns the start of the projection region.
 int proj_scratch(const mlra_desc* d, void* workspace, size_t ws_bytes, void** scratch) {
@@ -588,6 +700,14 @@ int proj_scratch(const mlra_desc* d, void* workspace, size_t ws_bytes, void** sc
 size_t mlra::proj_scratch_bytes(const mlra_desc* d) {
   if (!elems_bf16(d) || d->d_model < 1 || d->d_model % 8 != 0) return 0;  // VALU path: no scratch
   size_t need = 0;
+  if (d->d_c % 8 == 0 && d->d_r % 8 == 0) {
+    need = std::max(need, proj_mfma_scratch_bytes(
+                              append_batch(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), kCplToken));
+    if (d->d_cq % 8 == 0)
+      need = std::max(need, proj_mfma_scratch_bytes(token_batch(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                                nullptr, nullptr, nullptr, nullptr),
+                                                    kCplToken));
+  }
   if (d->d_r > 0 && d->d_r % 8 == 0)
     need = std::max(need, proj_mfma_scratch_bytes(rope_batch(d, nullptr, nullptr, nullptr, nullptr), kCplRope));
   if (d->d_cq > 0 && d->d_cq % 8 == 0 && d->d_h % 8 == 0 && d->d_r % 8 == 0) {
@@ -701,4 +821,53 @@ extern "C" int mlra_project_query(const mlra_desc* desc, const void* x, const vo
   a.rope = 1;
   a.rope_base = rope_base_of(desc);
   return proj_status(launch_proj(a, desc->n_heads, s));
+}
+
+// Latent append on the MFMA path (bf16 x and W^DKV, d_model % 8 == 0, 16-byte
+// aligned arrays); returns kNotEligible for the fp32 kernel's inputs.
+int mlra::append_latent_mfma(const mlra_desc* desc, void* pool, const int32_t* page_table,
+                             const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
+                             void* c_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!mfma_path(desc, {x, w_dkv, kr_new, c_out}) || desc->d_c % 8 != 0 || desc->d_r % 8 != 0) return kNotEligible;
+  void* scratch = nullptr;
+  const int st = proj_scratch(desc, workspace, ws_bytes, &scratch);
+  if (st != MLRA_OK) return st;
+  ProjBatch b = append_batch(desc, x, w_dkv, positions, pool, page_table, kr_new, c_out);
+  return proj_status(launch_proj_mfma(b, kCplToken, scratch, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int mlra_project_token(const mlra_desc* desc, const void* x, const int32_t* positions, void* pool,
+                                  const int32_t* page_table, const void* w_dkv, const void* w_kr, void* kr_out,
+                                  void* c_out, const void* w_dq, const void* w_uq, const void* w_qr, float* c_q,
+                                  void* q_c, void* q_r, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace mlra;
+  int st = check_desc(desc, nullptr);
+  if (st != MLRA_OK) return st;
+  if (desc->d_model < 1 || desc->d_cq < 0) return MLRA_ERR_INVALID_ARG;
+  if (!x || !positions || !pool || !w_dkv || (desc->d_r > 0 && (!w_kr || !kr_out))) return MLRA_ERR_INVALID_ARG;
+  if (desc->d_cq > 0 && (!w_dq || !w_uq || !c_q || !q_c || (desc->d_r > 0 && (!w_qr || !q_r))))
+    return MLRA_ERR_INVALID_ARG;
+  if (!aligned16(w_dkv) || (w_kr && !aligned16(w_kr)) || (w_dq && !aligned16(w_dq)) || (w_uq && !aligned16(w_uq)) ||
+      (w_qr && !aligned16(w_qr)))
+    return MLRA_ERR_INVALID_ARG;
+  if (desc->d_r % 8 != 0 || desc->d_cq % 8 != 0 || desc->d_h % 8 != 0) return MLRA_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  st = proj_scratch(desc, workspace, ws_bytes, &scratch);
+  if (st != MLRA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!mfma_path(desc, {x, kr_out, c_out, c_q, q_c, q_r}) || desc->d_c % 8 != 0) {
+    // the fp32 kernels, one product at a time
+    if (desc->d_r > 0) {
+      st = mlra_rope_key(desc, x, w_kr, positions, kr_out, workspace, ws_bytes, stream);
+      if (st != MLRA_OK) return st;
+    }
+    st = mlra_append_latent(desc, pool, page_table, positions, x, w_dkv, kr_out, c_out, workspace, ws_bytes, stream);
+    if (st != MLRA_OK || desc->d_cq == 0) return st;
+    return mlra_project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, workspace, ws_bytes, stream);
+  }
+  ProjBatch b1 = token_batch(desc, x, positions, pool, page_table, w_dkv, w_kr, kr_out, c_out, w_dq, c_q);
+  st = proj_status(launch_proj_mfma(b1, kCplToken, scratch, s));
+  if (st != MLRA_OK || desc->d_cq == 0) return st;
+  ProjBatch b2 = query_batch2(desc, c_q, w_uq, w_qr, positions, q_c, q_r);
+  return proj_status(launch_proj_mfma(b2, kCplQuery2, scratch, s));
 }

@@ -124,10 +124,17 @@ size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len);
  *   magnitudes of 448 and above saturate to 448, NaN to 0x7F); c_out receives
  *   the fp32 latent before encoding.
  * A position outside [0, max_pages_per_seq * page_size) writes nothing. The
- * caller advances its sequence lengths itself. */
+ * caller advances its sequence lengths itself.
+ * workspace: at least mlra_workspace_bytes(desc, .) bytes (the decode's
+ * workspace, which then also holds this call's split-K scratch; calls sharing
+ * it must be ordered on one stream), else MLRA_ERR_WORKSPACE. With bf16
+ * arrays, d_model % 8 == 0 and 16-byte aligned x, kr_new and c_out the product
+ * runs on MFMA (bf16 operands, fp32 accumulation); otherwise on an fp32 VALU
+ * kernel. */
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,
                        const int32_t* positions, const void* x, const void* w_dkv,
-                       const void* kr_new, void* c_out, void* stream);
+                       const void* kr_new, void* c_out, void* workspace, size_t ws_bytes,
+                       void* stream);
 
 /* Query absorption (lesty.tech section 5; ai360xpert "Absorbing the
  * up-projection") and work planning:
@@ -207,6 +214,19 @@ int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
 int mlra_project_query(const mlra_desc* desc, const void* x, const void* w_dq, const void* w_uq,
                        const void* w_qr, const int32_t* positions, float* c_q, void* q_c,
                        void* q_r, void* workspace, size_t ws_bytes, void* stream);
+
+/* Everything the new token's hidden state x feeds before the attention, in
+ * one call: the same results as mlra_rope_key (into kr_out), then
+ * mlra_append_latent with kr_new = kr_out, then (d_cq > 0) mlra_project_query.
+ * On the MFMA path the three products over x (W^DKV, W^KR, W^DQ) share one
+ * launch and the pool row, k^R and c^Q are written by its epilogue; the query
+ * up-projections take a second launch. w_dq, w_uq, w_qr, c_q, q_c and q_r may
+ * be NULL when d_cq == 0; c_out may be NULL. Same layouts, element types and
+ * workspace as the three calls. */
+int mlra_project_token(const mlra_desc* desc, const void* x, const int32_t* positions, void* pool,
+                       const int32_t* page_table, const void* w_dkv, const void* w_kr, void* kr_out,
+                       void* c_out, const void* w_dq, const void* w_uq, const void* w_qr, float* c_q,
+                       void* q_c, void* q_r, void* workspace, size_t ws_bytes, void* stream);
 
 /* Copies the workspace's error flags (MLRA_FLAG_*) to *flags (host memory),
  * after the work already enqueued on `stream` (synchronises it). The flags are

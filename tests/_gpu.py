@@ -61,7 +61,7 @@ class GpuProblem:
 
     def append(self, stream=None):
         mlra.append_latent(self.desc, self.pool, self.page_table, self.positions, self.x, self.w_dkv,
-                           self.kr_new, self.c_out, stream)
+                           self.kr_new, self.c_out, self.ws, stream)
 
     def step(self, stream=None):
         mlra.decode(self.desc, self.pool, self.page_table, self.seq_lens, self.max_seq_len, self.q_c,

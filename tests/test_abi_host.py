@@ -123,15 +123,41 @@ def test_combine_and_append_validation():
     assert L.mlra_combine(ctypes.byref(d), None, 1 << 30, FAKE, FAKE, None, None) == mlra.ERR_INVALID_ARG
     assert L.mlra_combine(ctypes.byref(d), FAKE, 1 << 30, FAKE, None, None, None) == mlra.ERR_INVALID_ARG
     # append needs d_model >= 1
-    assert L.mlra_append_latent(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == \
-        mlra.ERR_INVALID_ARG
+    A = L.mlra_append_latent
+    ws = (FAKE, ctypes.c_size_t(16), None)  # a workspace far too small: nothing valid gets past it
+    assert A(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, *ws) == mlra.ERR_INVALID_ARG
     d2 = _desc(d_model=32)
-    assert L.mlra_append_latent(ctypes.byref(d2), None, None, FAKE, FAKE, FAKE, FAKE, None, None) == \
-        mlra.ERR_INVALID_ARG
-    assert L.mlra_append_latent(ctypes.byref(d2), FAKE, None, FAKE, FAKE, FAKE, None, None, None) == \
+    assert A(ctypes.byref(d2), None, None, FAKE, FAKE, FAKE, FAKE, None, *ws) == mlra.ERR_INVALID_ARG
+    assert A(ctypes.byref(d2), FAKE, None, FAKE, FAKE, FAKE, None, None, *ws) == \
         mlra.ERR_INVALID_ARG  # k^R_new required when d_r > 0
-    assert L.mlra_append_latent(ctypes.byref(d2), FAKE, None, FAKE, FAKE, ctypes.c_void_p(0x1008), FAKE,
-                                None, None) == mlra.ERR_INVALID_ARG  # W^DKV not 16-byte aligned
+    assert A(ctypes.byref(d2), FAKE, None, FAKE, FAKE, ctypes.c_void_p(0x1008), FAKE, None, *ws) == \
+        mlra.ERR_INVALID_ARG  # W^DKV not 16-byte aligned
+    # the workspace is part of the contract on every path
+    assert A(ctypes.byref(d2), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, ctypes.c_size_t(1 << 30), None) == \
+        mlra.ERR_INVALID_ARG
+    d3 = _desc(d_model=32, dtype="bf16", n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16)
+    assert A(ctypes.byref(d3), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, *ws) == mlra.ERR_WORKSPACE
+
+
+def test_project_token_validation():
+    L = mlra.lib()
+    d = _desc(d_model=64, d_cq=32, dtype="bf16")
+
+    def call(desc=d, x=FAKE, pos=FAKE, pool=FAKE, wdkv=FAKE, wkr=FAKE, kr=FAKE, wdq=FAKE, wuq=FAKE, wqr=FAKE,
+             cq=FAKE, qc=FAKE, qr=FAKE, ws=FAKE, ws_bytes=16):
+        return L.mlra_project_token(ctypes.byref(desc), x, pos, pool, None, wdkv, wkr, kr, None, wdq, wuq, wqr,
+                                    cq, qc, qr, ws, ctypes.c_size_t(ws_bytes), None)
+
+    for k in ("x", "pos", "pool", "wdkv", "wkr", "kr", "wdq", "wuq", "wqr", "cq", "qc", "qr"):
+        assert call(**{k: None}) == mlra.ERR_INVALID_ARG, k
+    for k in ("wdkv", "wkr", "wdq", "wuq", "wqr"):
+        assert call(**{k: ctypes.c_void_p(0x1004)}) == mlra.ERR_INVALID_ARG, k
+    assert call() == mlra.ERR_WORKSPACE
+    assert call(ws=None) == mlra.ERR_INVALID_ARG
+    # no query path: its arrays may be NULL
+    nq = _desc(d_model=64, dtype="bf16")
+    assert call(desc=nq, wdq=None, wuq=None, wqr=None, cq=None, qc=None, qr=None) == mlra.ERR_WORKSPACE
+    assert call(desc=_desc(d_model=0, d_cq=32, dtype="bf16")) == mlra.ERR_INVALID_ARG
 
 
 def test_read_flags_validation():

@@ -125,7 +125,7 @@ def test_whole_step_chained_on_device():
                        _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr, prob.ws)
     mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr, prob.ws)
     mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr,
-                       None)
+                       None, prob.ws)
     mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
                 prob.w_uk, prob.ws)
     mlra.combine(desc, prob.ws, prob.w_uv, prob.out, prob.lse)
@@ -168,7 +168,7 @@ def test_full_size_layer_workload():
     mlra.project_query(desc, prob.x, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
                        _gpu.to_dev(inp.w_qr), prob.positions, cq, qc, qr, prob.ws)
     mlra.rope_key(desc, prob.x, _gpu.to_dev(inp.w_kr), prob.positions, kr, prob.ws)
-    mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr, None)
+    mlra.append_latent(desc, prob.pool, prob.page_table, prob.positions, prob.x, prob.w_dkv, kr, None, prob.ws)
     mlra.decode(desc, prob.pool, prob.page_table, prob.seq_lens, prob.max_seq_len, qc, qr,
                 prob.w_uk, prob.ws)
     mlra.combine(desc, prob.ws, prob.w_uv, prob.out, prob.lse)
@@ -191,3 +191,57 @@ def test_full_size_layer_workload():
     ref, _ = oracle.decode_unabsorbed(inp, pairs)
     err = _gpu.check_outputs(np.stack([out[b, i] for b, i in pairs]), ref, "bf16")
     _say(f"  full-size layer step: out max err/rms {err:.2e}")
+
+
+@pytest.mark.parametrize("name", ["bf16-mlra4", "bf16-wide", "fp8-cache"])
+def test_project_token_fused(name):
+    """mlra_project_token: the latent append, the RoPE key and the query path
+    of the new token in one call. k^R, q^C and q^R against the oracle; the
+    appended row's latent within one bf16 ulp of the oracle's (FP8: the codes
+    of the kernel's own fp32 latent, which is within 1e-5 of the oracle's);
+    the row's RoPE part equal to k^R; every other pool byte unchanged."""
+    _say(f"case: project_token {name}")
+    t = _gpu.torch()
+    s, inp = _problem(name)
+    prob = _gpu.GpuProblem(inp)
+    desc = prob.desc
+    et = mlra._elem_dtype(desc)
+    fp8 = s.dtype == "fp8"
+    cq = t.empty((s.batch, s.d_cq), dtype=t.float32, device="cuda")
+    qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
+    qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
+    kr = t.empty((s.batch, s.d_r), dtype=et, device="cuda")
+    c_out = t.empty((s.batch, s.d_c), dtype=t.float32 if fp8 else et, device="cuda")
+    before = _gpu.from_dev_bits(prob.pool).copy()
+    mlra.project_token(desc, prob.x, prob.positions, prob.pool, prob.page_table, prob.w_dkv,
+                       _gpu.to_dev(inp.w_kr), kr, c_out, _gpu.to_dev(inp.w_dq), _gpu.to_dev(inp.w_uq),
+                       _gpu.to_dev(inp.w_qr), cq, qc, qr, prob.ws)
+    t.cuda.synchronize()
+    after = _gpu.from_dev_bits(prob.pool)
+    kr_b = _gpu.from_dev_bits(kr)
+    _check(_bits_to_f64(kr_b, s.arrays_dtype), oracle.rope_key(inp), s.arrays_dtype, "k^R")
+    ref_c, ref_r = oracle.project_query(inp)
+    _check(_bits_to_f64(_gpu.from_dev_bits(qc), s.arrays_dtype), ref_c, s.arrays_dtype, "q^C")
+    _check(_bits_to_f64(_gpu.from_dev_bits(qr), s.arrays_dtype), ref_r, s.arrays_dtype, "q^R")
+    # the oracle's append with the device's k^R
+    inp.kr_new = kr_b
+    c_ref = oracle.append(inp, inp.pool.copy())
+    c_gpu = _gpu.from_dev_bits(c_out)
+    P = s.page_size
+    changed = np.zeros(before.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // P], pos % P
+        changed[pg, off] = True
+        row = after[pg, off]
+        if fp8:
+            err = np.abs(c_gpu[b].astype(np.float64) - c_ref[b]) / max(_gpu.rms(c_ref), 1e-30)
+            assert err.max() <= 1e-5, err.max()
+            codes = oracle.e4m3_encode_array(c_gpu[b] * np.float32(1.0 / s.cache_scale))
+            assert np.array_equal(row[:s.d_c], codes)
+            assert np.array_equal(row[s.d_c:].view(np.uint16), kr_b[b])
+        else:
+            assert np.abs(c_gpu[b].astype(np.int32) - c_ref[b].astype(np.int32)).max() <= 1
+            assert np.array_equal(row[:s.d_c], c_gpu[b])
+            assert np.array_equal(row[s.d_c:], kr_b[b])
+    assert np.array_equal(before[~changed], after[~changed])
