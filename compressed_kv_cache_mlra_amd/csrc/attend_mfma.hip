@@ -254,11 +254,12 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // the whole tile sits in one page: one base, per-lane offsets
       const uint8_t* base = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(
           pool + (static_cast<int64_t>(page_of(x, 0)) * P + (tok0 & (P - 1))) * C::ROWG)));
+      // rows are contiguous inside a page: chunk p of the tile is at 16 p, a
+      // 32-bit offset from the uniform base (scalar base + vector offset)
 #pragma unroll
       for (int k = 0; k < C::NL; ++k) {
-        const int p = k * C::NLT + tid;
-        const int r = p / C::CPRG, lc = p % C::CPRG;
-        ring[k] = gload16_stream(base + r * C::ROWG + 16 * lc);
+        const uint32_t off = 16u * static_cast<uint32_t>(k * C::NLT + tid);
+        ring[k] = gload16_stream(base + off);
       }
     } else {
       // tile spans npt pages (tok0 is page aligned): per-lane page select
