@@ -650,15 +650,15 @@ constexpr Entry entry() {
 }
 
 // Shapes with a tuned MFMA kernel. Key: (w, d_r, blocks per row, 16-head tiles per block).
-// Step order (last flag, compute-first): measured per shape on one box, same
-// binary A/B: compute-first is 4-7% faster for the TP-share, MLRA-2 and FP8
-// MLRA-4 kernels and 6-7% slower for bf16 MLRA-4 and MLA; the FP8 TP-share and
-// MLRA-2 kernels follow their bf16 counterparts.
+// Step order (compute-first flag): measured per shape on one box, same
+// binary A/B: compute-first is 4-7% faster for the TP-share, MLRA-2, FP8
+// MLRA-4 and column-split MLA kernels and 2-6% slower for bf16 MLRA-4; the FP8
+// TP-share and MLRA-2 kernels follow their bf16 counterparts.
 const Entry kVariants[] = {
     entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
     // MLA: one 512 latent, 64 heads; column-split waves (half the value
-    // columns and half the score dimensions each): 6% faster than unsplit
-    entry<512, 64, 1, 4, 1, 32, 1, false, false, 2>(),
+    // columns and half the score dimensions each), compute-first
+    entry<512, 64, 1, 4, 1, 32, 1, false, true, 2>(),
     // one MLRA-4 block (a TP rank's share), <= 16 heads: one-wave workgroups,
     // four per compute unit, each streaming its own 32-token tiles (measured
     // 1.8x faster than four waves sharing 128-token tiles at one per unit)
