@@ -43,7 +43,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false, bool CF_ = false,
-          int CS_ = 1>
+          int CS_ = 1, bool P2_ = false>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -63,6 +63,10 @@ struct Cfg {
   // the query dimensions; the partial scores are summed through LDS. This
   // divides the accumulator and query registers by CS.
   static constexpr int CS = CS_;
+  // Prologue: P2 requests the unit's first two tiles together (a second
+  // register set, live only before the loop); otherwise the second is
+  // requested once the first is in LDS. Chosen per shape by measurement.
+  static constexpr bool P2 = P2_;
   static constexpr int ROWB = ROW * 2;  // bytes of a row in LDS (bf16 throughout)
   static constexpr int CPR = ROW / 8;   // 16-byte LDS chunks per row
   static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROWB;  // bytes of a row in HBM
@@ -356,8 +360,13 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   // ---- prologue: with the descriptor in hand, tile x0 (its page looked up
   // with a scalar load), the query and the page ids of the rest of the unit
   // are requested together; tile x0+1 follows once x0 is in LDS.
-  u32x4_t ring[C::NL];
-  load_tile(x0, ring);
+  u32x4_t ring0[C::P2 ? C::NL : 1], ring[C::NL];
+  if constexpr (C::P2) {
+    load_tile(x0, ring0);
+    if (x0 + 1 < x1) load_tile(x0 + 1, ring);
+  } else {
+    load_tile(x0, ring);
+  }
 
   const int32_t nx_end = cload(ud + 6), nx_n = cload(ud + 7);  // the sequence after lo
   const int32_t ntab = (x1 - x0) * npt;
@@ -402,8 +411,12 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     }
     __syncthreads();
   }
-  store_tile(ring, lds, store_valid(x0));
-  if (x0 + 1 < x1) load_tile(x0 + 1, ring);
+  if constexpr (C::P2) {
+    store_tile(ring0, lds, store_valid(x0));
+  } else {
+    store_tile(ring, lds, store_valid(x0));
+    if (x0 + 1 < x1) load_tile(x0 + 1, ring);
+  }
 
   auto step = [&](int32_t x) __attribute__((always_inline)) {
     const int t = x - x0;
@@ -642,9 +655,10 @@ struct Entry {
   hipError_t (*fn)(const DecodeArgs&, hipStream_t);
 };
 
-template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1>
+template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1,
+          bool P2 = false>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS>;
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2>;
   return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? 1 : 0, C::NTHREADS, 2 * C::TILE_BYTES},
                &run_variant<C>};
 }
@@ -653,7 +667,9 @@ constexpr Entry entry() {
 // Step order (compute-first flag): measured per shape on one box, same
 // binary A/B: compute-first is 4-7% faster for the TP-share, MLRA-2, FP8
 // MLRA-4 and column-split MLA kernels and 2-6% slower for bf16 MLRA-4; the FP8
-// TP-share and MLRA-2 kernels follow their bf16 counterparts.
+// TP-share and MLRA-2 kernels follow their bf16 counterparts. Two-tile
+// prologue (last flag): 4-6% faster for the TP-share and FP8 MLRA-4 kernels,
+// 22% for MLRA-2, slower for bf16 MLRA-4 (3%) and MLA (45%: its registers).
 const Entry kVariants[] = {
     entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
     // MLA: one 512 latent, 64 heads; column-split waves (half the value
@@ -662,16 +678,16 @@ const Entry kVariants[] = {
     // one MLRA-4 block (a TP rank's share), <= 16 heads: one-wave workgroups,
     // four per compute unit, each streaming its own 32-token tiles (measured
     // 1.8x faster than four waves sharing 128-token tiles at one per unit)
-    entry<128, 64, 1, 1, 1, 32, 4, false, true>(),
+    entry<128, 64, 1, 1, 1, 32, 4, false, true, 1, true>(),
     // MLRA-2: 2 x 256 latent, <= 32 heads per block; column-split waves, one
-    // workgroup per compute unit (no spills; 2.8% faster than two
-    // workgroups of unsplit waves)
-    entry<256, 64, 2, 2, 1, 32, 1, false, true, 2>(),
+    // workgroup per compute unit (no spills), two-tile prologue: the fastest
+    // step of the four combinations of split and prologue measured
+    entry<256, 64, 2, 2, 1, 32, 1, false, true, 2, true>(),
     entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
     entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
     entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
     // FP8 (E4M3FN) caches of the same shapes and tunings
-    entry<128, 64, 4, 1, 1, 32, 2, true, true>(),
+    entry<128, 64, 4, 1, 1, 32, 2, true, true, 1, true>(),
     entry<512, 64, 1, 4, 1, 32, 1, true>(),
     entry<128, 64, 1, 1, 1, 32, 4, true, true>(),
     entry<256, 64, 2, 2, 1, 32, 2, true, true>(),
