@@ -175,14 +175,17 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_kernel(DecodeArgs a, co
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kAbsorbMaxKD = 16;       // d_h / 32 for d_h <= 512
+constexpr int kAbsorbTilesPerWg = 8;   // 16-row W^UK tiles per workgroup (grid z splits the rest)
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 absorption on MFMA: for head-block pair hk and a 16-sequence tile,
 //   D[c][b] = sum_d W^UK[hk][c][d] q^C[b][head][d]   (v_mfma_f32_16x16x32_bf16)
 // with W^UK rows as the A operand and queries as the B operand, both read
-// straight from global memory 16 bytes per lane. grid: (hk, ceil(batch / 16) + 1),
-// the last row being the plan row.
+// straight from global memory 16 bytes per lane (the query operands once per
+// lane). grid: (hk, ceil(batch / 16) + 1, ceil(w / 128)): z splits the 16-row
+// tiles of W^UK eight to a workgroup; the last y row is the plan row.
 __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs a, const int32_t* seq_lens,
                                                                       const uint16_t* __restrict__ q_c,
                                                                       const uint16_t* __restrict__ q_r,
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
   const int HK = a.n_heads * a.k;
   const int QW = a.w + a.d_r;
   if (blockIdx.y == gridDim.y - 1) {  // the plan row: one workgroup plans
-    if (blockIdx.x == 0) plan_block(a, seq_lens);
+    if (blockIdx.x == 0 && blockIdx.z == 0) plan_block(a, seq_lens);
     return;
   }
 
@@ -204,20 +207,31 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
   const uint16_t* qrow = q_c + (static_cast<int64_t>(b) * a.n_heads + head) * a.d_h;
   const uint16_t* wbase = w_uk + static_cast<int64_t>(hk) * a.w * a.d_h;
   uint16_t* qext = reinterpret_cast<uint16_t*>(a.ws + a.off_qext);
+  // the query operands of this lane's sequence, loaded once (d_h <= 512)
+  const int KD = (a.d_h + 31) / 32;
+  u32x4_t bq[kAbsorbMaxKD];
+#pragma unroll
+  for (int kk = 0; kk < kAbsorbMaxKD; ++kk) {
+    const int d = 32 * kk + 8 * g4;
+    bq[kk] = (kk < KD && d < a.d_h && b_ok) ? *reinterpret_cast<const u32x4_t*>(qrow + d) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // this workgroup's 16-row tiles of W^UK: kAbsorbTilesPerWg of them, one per wave at a time
   const int n_mt = a.w / 16;
-  for (int mt = wave; mt < n_mt; mt += kAbsorbThreads / 64) {
+  const int mt_end = min(n_mt, static_cast<int>(blockIdx.z + 1) * kAbsorbTilesPerWg);
+  for (int mt = blockIdx.z * kAbsorbTilesPerWg + wave; mt < mt_end; mt += kAbsorbThreads / 64) {
     floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
     const uint16_t* wrow = wbase + static_cast<int64_t>(mt * 16 + m16) * a.d_h;
-    for (int d0 = 0; d0 < a.d_h; d0 += 32) {
-      const int d = d0 + 8 * g4;
-      u32x4_t av = u32x4_t{0u, 0u, 0u, 0u}, bv = av;
-      if (d < a.d_h) {
-        av = *reinterpret_cast<const u32x4_t*>(wrow + d);
-        if (b_ok) bv = *reinterpret_cast<const u32x4_t*>(qrow + d);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+    u32x4_t aw[kAbsorbMaxKD];
+#pragma unroll
+    for (int kk = 0; kk < kAbsorbMaxKD; ++kk) {
+      const int d = 32 * kk + 8 * g4;
+      aw[kk] = (kk < KD && d < a.d_h) ? *reinterpret_cast<const u32x4_t*>(wrow + d) : u32x4_t{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int kk = 0; kk < kAbsorbMaxKD; ++kk)
+      if (kk < KD)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw[kk]),
+                                                      __builtin_bit_cast(bf16x8_t, bq[kk]), acc, 0, 0, 0);
     if (b_ok) {
       // lane holds rows c = mt*16 + 4 g4 + i of sequence b: 4 consecutive outputs
       // the latent part carries the FP8 cache scale (1 otherwise)
@@ -230,6 +244,7 @@ __global__ __launch_bounds__(kAbsorbThreads) void absorb_mfma_kernel(DecodeArgs 
       *dst = make_uint2(lo, hi);
     }
   }
+  if (blockIdx.z != 0) return;  // the RoPE part once per (head-block pair, 16 sequences)
   const int nb = min(16, a.batch - b0);
   for (int e = tid; e < nb * a.d_r; e += kAbsorbThreads) {
     const int bl = e / a.d_r, r = e % a.d_r;
@@ -247,7 +262,9 @@ hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int3
   const size_t sh = sizeof(float) * kAbsorbBatchGroup * a.d_h;
   if (dtype == 1) {
     if (q_bf16 && a.d_h % 8 == 0 && a.w % 16 == 0)
-      absorb_mfma_kernel<<<dim3(a.n_heads * a.k, (a.batch + 15) / 16 + 1), kAbsorbThreads, 0, stream>>>(
+      absorb_mfma_kernel<<<dim3(a.n_heads * a.k, (a.batch + 15) / 16 + 1,
+                                (a.w / 16 + kAbsorbTilesPerWg - 1) / kAbsorbTilesPerWg),
+                           kAbsorbThreads, 0, stream>>>(
           a, seq_lens, static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
           static_cast<const uint16_t*>(w_uk));
     else if (q_bf16)

@@ -254,7 +254,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 //     row residues are summed with lane swaps inside a wave and through LDS
 //     across the four waves.
 constexpr int kFastThreads = 256;
-constexpr int kFastSeq = 4;     // sequences per workgroup
+// sequences per workgroup (a multiple of 4; 8 measured slower on every
+// workload: fewer workgroups outweigh the fewer W^UV re-reads)
+constexpr int kFastSeq = 4;
 constexpr int kFastSlots = 12;  // partial slots per half whose loads are in flight together
 constexpr int kFastDh = 128;
 
@@ -394,8 +396,15 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int e = rr + 16 * (i0 + i);
-      const float4 o = *reinterpret_cast<const float4*>(&ot[e][0]);
-      const float ov[4] = {o.x, o.y, o.z, o.w};
+      float ov[kFastSeq];
+#pragma unroll
+      for (int h = 0; h < kFastSeq / 4; ++h) {
+        const float4 o = *reinterpret_cast<const float4*>(&ot[e][4 * h]);
+        ov[4 * h] = o.x;
+        ov[4 * h + 1] = o.y;
+        ov[4 * h + 2] = o.z;
+        ov[4 * h + 3] = o.w;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t u = wr[i][q];
@@ -416,8 +425,10 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
   if (lane < 16) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<float4*>(&red[wave][dc][j][0]) =
-          make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+#pragma unroll
+      for (int h = 0; h < kFastSeq / 4; ++h)
+        *reinterpret_cast<float4*>(&red[wave][dc][j][4 * h]) =
+            make_float4(acc[j][4 * h], acc[j][4 * h + 1], acc[j][4 * h + 2], acc[j][4 * h + 3]);
   }
   __syncthreads();
   // outputs: f = (bl, d), d fastest
