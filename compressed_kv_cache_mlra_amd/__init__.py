@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmlra.so")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class MlraError(RuntimeError):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.mlra_attend.argtypes = [dp, vp, ip, vp, ctypes.c_size_t, vp]
         L.mlra_decode.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.mlra_decode_step.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
         L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
         L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp, ctypes.c_size_t, vp]
@@ -303,6 +305,25 @@ def combine(desc, workspace, w_uv, out, lse=None, stream=None):
         _ptr(out, kind="f32", name="out", numel=B * H * desc.d_h),
         _ptr(lse, kind="f32", name="lse", numel=B * H * K, nullable=True),
         _stream(stream)), "combine")
+
+
+def decode_step(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, w_uv, out, workspace, lse=None,
+                stream=None):
+    """absorb_query + attend + combine in one call."""
+    B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
+    _check(lib().mlra_decode_step(
+        ctypes.byref(desc),
+        _pool_ptr(pool, desc),
+        _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
+        _ptr(seq_lens, kind="int32", name="seq_lens", numel=B), ctypes.c_int32(int(max_seq_len)),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=desc.d_r == 0),
+        _ptr(w_uk, desc, name="w_uk", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(w_uv, desc, name="w_uv", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(out, kind="f32", name="out", numel=B * H * desc.d_h),
+        _ptr(lse, kind="f32", name="lse", numel=B * H * K, nullable=True),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        _stream(stream)), "decode_step")
 
 
 def read_flags(workspace, stream=None) -> int:

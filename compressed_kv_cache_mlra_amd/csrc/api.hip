@@ -140,6 +140,32 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   return a;
 }
 
+CombineArgs combine_args(const mlra_desc* d, const Plan& p, const void* ws, const void* w_uv, float* out,
+                         float* lse) {
+  CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.ws = static_cast<const char*>(ws);
+  c.w_uv = w_uv;
+  c.out = out;
+  c.lse = lse;
+  c.off_sunit = static_cast<int64_t>(p.off_sunit);
+  c.off_pm = static_cast<int64_t>(p.off_pm);
+  c.off_pl = static_cast<int64_t>(p.off_pl);
+  c.off_po = static_cast<int64_t>(p.off_po);
+  c.po_f16 = p.variant ? 1 : 0;
+  c.batch = d->batch;
+  c.n_heads = d->n_heads;
+  c.d_h = d->d_h;
+  c.w = p.s.w;
+  c.k = d->blocks_per_head;
+  c.hk = p.s.hk;
+  c.groups = p.groups;
+  c.empty_slot = static_cast<int32_t>(p.slots - 1);
+  c.out_scale = d->out_scale > 0.f ? d->out_scale : 1.0f / sqrtf(static_cast<float>(d->blocks_per_head));
+  c.out_scale *= cache_scale_of(d);  // FP8 caches: the partials sum codes, not latent values
+  return c;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MLRA_OK : MLRA_ERR_HIP; }
 
 // Element type of queries, weights and append inputs (bf16 for FP8 caches).
@@ -152,7 +178,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 5; }
+int mlra_abi_version(void) { return 6; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -224,28 +250,26 @@ int mlra_combine(const mlra_desc* desc, const void* workspace, size_t ws_bytes, 
   if (st != MLRA_OK) return st;
   if (!workspace || !w_uv || !out) return MLRA_ERR_INVALID_ARG;
   if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
-  CombineArgs c;
-  memset(&c, 0, sizeof(c));
-  c.ws = static_cast<const char*>(workspace);
-  c.w_uv = w_uv;
-  c.out = out;
-  c.lse = lse;
-  c.off_sunit = static_cast<int64_t>(p.off_sunit);
-  c.off_pm = static_cast<int64_t>(p.off_pm);
-  c.off_pl = static_cast<int64_t>(p.off_pl);
-  c.off_po = static_cast<int64_t>(p.off_po);
-  c.po_f16 = p.variant ? 1 : 0;
-  c.batch = desc->batch;
-  c.n_heads = desc->n_heads;
-  c.d_h = desc->d_h;
-  c.w = p.s.w;
-  c.k = desc->blocks_per_head;
-  c.hk = p.s.hk;
-  c.groups = p.groups;
-  c.empty_slot = static_cast<int32_t>(p.slots - 1);
-  c.out_scale = desc->out_scale > 0.f ? desc->out_scale
-                                      : 1.0f / sqrtf(static_cast<float>(desc->blocks_per_head));
-  c.out_scale *= cache_scale_of(desc);  // FP8 caches: the partials sum codes, not latent values
+  const CombineArgs c = combine_args(desc, p, workspace, w_uv, out, lse);
+  return hip_status(launch_combine(c, arrays_dtype(desc), static_cast<hipStream_t>(stream)));
+}
+
+int mlra_decode_step(const mlra_desc* desc, const void* pool, const int32_t* page_table,
+                     const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
+                     const void* w_uk, const void* w_uv, float* out, float* lse, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!pool || !seq_lens || !q_c || !w_uk || !w_uv || !out || !workspace || (desc->d_r > 0 && !q_r))
+    return MLRA_ERR_INVALID_ARG;
+  if (max_seq_len < 0 || static_cast<int64_t>(max_seq_len) >
+                             static_cast<int64_t>(desc->max_pages_per_seq) * desc->page_size)
+    return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  const CombineArgs c = combine_args(desc, p, workspace, w_uv, out, lse);
+  st = mlra_decode(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, workspace, ws_bytes, stream);
+  if (st != MLRA_OK) return st;
   return hip_status(launch_combine(c, arrays_dtype(desc), static_cast<hipStream_t>(stream)));
 }
 

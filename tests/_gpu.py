@@ -68,8 +68,13 @@ class GpuProblem:
                     self.q_r, self.w_uk, self.ws, stream)
         mlra.combine(self.desc, self.ws, self.w_uv, self.out, self.lse, stream)
 
-    def run(self, stream=None):
-        self.step(stream)
+    def step_one_call(self, stream=None):
+        """The whole step through mlra_decode_step."""
+        mlra.decode_step(self.desc, self.pool, self.page_table, self.seq_lens, self.max_seq_len, self.q_c,
+                         self.q_r, self.w_uk, self.w_uv, self.out, self.ws, self.lse, stream)
+
+    def run(self, stream=None, one_call=False):
+        (self.step_one_call if one_call else self.step)(stream)
         torch().cuda.synchronize()
         return self.out.cpu().numpy().astype(np.float64), self.lse.cpu().numpy().astype(np.float64)
 

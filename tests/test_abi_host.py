@@ -139,6 +139,26 @@ def test_combine_and_append_validation():
     assert A(ctypes.byref(d3), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, *ws) == mlra.ERR_WORKSPACE
 
 
+def test_decode_step_validation():
+    """The one-call step checks everything the three calls it stands for check."""
+    L = mlra.lib()
+    d = _desc()
+    need = mlra.workspace_bytes(d, 100)
+
+    def step(pool=FAKE, seq_lens=FAKE, max_seq_len=100, q_c=FAKE, q_r=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE,
+             lse=None, ws=FAKE, ws_bytes=need):
+        return L.mlra_decode_step(ctypes.byref(d), pool, None, seq_lens, max_seq_len, q_c, q_r, w_uk, w_uv, out,
+                                  lse, ws, ctypes.c_size_t(ws_bytes), None)
+
+    for field in ("pool", "seq_lens", "q_c", "q_r", "w_uk", "w_uv", "out", "ws"):
+        assert step(**{field: None}) == mlra.ERR_INVALID_ARG, field
+    assert step(max_seq_len=-1) == mlra.ERR_INVALID_ARG
+    assert step(max_seq_len=4 * 64 + 1) == mlra.ERR_INVALID_ARG
+    assert step(ws_bytes=need - 1) == mlra.ERR_WORKSPACE
+    assert L.mlra_decode_step(None, FAKE, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                              ctypes.c_size_t(need), None) == mlra.ERR_INVALID_ARG
+
+
 def test_project_token_validation():
     L = mlra.lib()
     d = _desc(d_model=64, d_cq=32, dtype="bf16")
