@@ -306,6 +306,11 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
   const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;
 
   // ---- merge
+  // lse values are stored after the outputs: a store issued here would be
+  // waited for (stores count in vmcnt) before the W^UV registers are used
+  constexpr int NIT = NITEMS / kFastThreads;
+  float lse_v[NIT];
+  int64_t lse_i[NIT];
   auto merge = [&](auto check_units) __attribute__((always_inline)) {
     constexpr bool kCheck = decltype(check_units)::value;
 #pragma unroll
@@ -363,10 +368,12 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
       const float r0 = fast_exp2(M - mu), r1 = fast_exp2(Mo - mu);
       const float Lt = L * r0 + Lo * r1;
       const float invL = nslots > 0 ? 1.f / Lt : 0.f;
+      lse_i[it0 / kFastThreads] = -1;
       if (half == 0) {
-        if (c == 0 && a.lse && bl < nb)
-          a.lse[(static_cast<int64_t>(b) * a.n_heads + head) * KB + jj] =
-              nslots > 0 ? 0.69314718055994531f * (Mt + __log2f(Lt)) : -INFINITY;
+        if (c == 0 && a.lse && bl < nb) {
+          lse_i[it0 / kFastThreads] = (static_cast<int64_t>(b) * a.n_heads + head) * KB + jj;
+          lse_v[it0 / kFastThreads] = nslots > 0 ? 0.69314718055994531f * (Mt + __log2f(Lt)) : -INFINITY;
+        }
         ot[e + 0][bl] = (acc.x * r0 + ao.x * r1) * invL;
         ot[e + 1][bl] = (acc.y * r0 + ao.y * r1) * invL;
         ot[e + 2][bl] = (acc.z * r0 + ao.z * r1) * invL;
@@ -442,6 +449,9 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
       a.out[(static_cast<int64_t>(b0 + bl) * a.n_heads + head) * kFastDh + d] = a.out_scale * v;
     }
   }
+#pragma unroll
+  for (int i = 0; i < NIT; ++i)
+    if (lse_i[i] >= 0) a.lse[lse_i[i]] = lse_v[i];
 }
 
 template <int W, int KB>
