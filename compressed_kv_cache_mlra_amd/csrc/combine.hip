@@ -250,9 +250,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 //     item take alternate partial slots (up to kFastSlots each per batch) and
 //     are merged with one lane exchange;
 //   * product: thread = (8 output columns, row residue r mod 16); its W^UV
-//     rows are requested with 16-byte loads before the merge starts; the 16
-//     row residues are summed with lane swaps inside a wave and through LDS
-//     across the four waves.
+//     rows are requested with 16-byte loads before the merge starts; each
+//     wave multiplies its rows on MFMA and the four waves are summed in LDS.
 constexpr int kFastThreads = 256;
 // sequences per workgroup (a multiple of 4; 8 measured slower on every
 // workload: fewer workgroups outweigh the fewer W^UV re-reads)
@@ -261,14 +260,9 @@ constexpr int kFastSlots = 12;  // partial slots per half whose loads are in fli
 constexpr int kFastDh = 128;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float sum_lanes_16_32_48(float v) {
-  // sum over lanes l, l^16, l^32, l^48
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+static_assert(kFastSeq == 4, "the product's lanes 0-15 carry four sequences");
 
 template <int W, int KB, bool PB>
 __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs a) {
@@ -387,12 +381,17 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
     merge(std::true_type{});
   __syncthreads();
 
-  // ---- product: acc[j][bl] = sum over this thread's rows of W^UV[e][8 dc + j] o~[bl][e]
-  float acc[8][kFastSeq];
+  // ---- product on MFMA: out[bl][d] = sum_e o~[bl][e] W^UV[e][d] with
+  // v_mfma_f32_16x16x32_bf16, the sequences as MFMA rows (kFastSeq of 16 used).
+  // A k-step of a wave covers the 32 rows e = rr + 16 i (rr = 4 wave + lane / 16,
+  // i = 8 s .. 8 s + 7) whose W^UV columns [8 dc, 8 dc + 8) this thread loaded:
+  // the columns are transposed in registers with v_perm_b32 (MFMA j, column dc
+  // = output column 8 dc + j), and o~ enters as bf16 hi + lo parts (about 16
+  // significant bits). Each wave sums its rows; the waves meet in LDS.
+  const int g4 = lane >> 4;
+  floatx4_t pacc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int bl = 0; bl < kFastSeq; ++bl) acc[j][bl] = 0.f;
+  for (int j = 0; j < 8; ++j) pacc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i0 = 0; i0 < ROWS; i0 += RB) {
     if (i0 > 0) {
@@ -401,41 +400,38 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
         wr[i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * (i0 + i)) * kFastDh);
     }
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int e = rr + 16 * (i0 + i);
-      float ov[kFastSeq];
+    for (int s8 = 0; s8 < RB; s8 += 8) {
+      // A: row dc is sequence dc (zero past kFastSeq), k = this lane's 8 rows
+      u32x4_t ahi, alo;
 #pragma unroll
-      for (int h = 0; h < kFastSeq / 4; ++h) {
-        const float4 o = *reinterpret_cast<const float4*>(&ot[e][4 * h]);
-        ov[4 * h] = o.x;
-        ov[4 * h + 1] = o.y;
-        ov[4 * h + 2] = o.z;
-        ov[4 * h + 3] = o.w;
+      for (int u = 0; u < 4; ++u) {
+        float v2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v2[h] = dc < kFastSeq ? ot[rr + 16 * (i0 + s8 + 2 * u + h)][dc] : 0.f;
+        const uint16_t h0 = f32_to_bf16(v2[0]), h1 = f32_to_bf16(v2[1]);
+        const uint16_t l0 = f32_to_bf16(v2[0] - bf16_to_f32(h0)), l1 = f32_to_bf16(v2[1] - bf16_to_f32(h1));
+        ahi[u] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        alo[u] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t u = wr[i][q];
-        const float wlo = __uint_as_float(u << 16), whi = __uint_as_float(u & 0xffff0000u);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t bv;
 #pragma unroll
-        for (int bl = 0; bl < kFastSeq; ++bl) {
-          acc[2 * q][bl] += wlo * ov[bl];
-          acc[2 * q + 1][bl] += whi * ov[bl];
-        }
+        for (int u = 0; u < 4; ++u) bv[u] = __builtin_amdgcn_perm(wr[s8 + 2 * u + 1][j >> 1], wr[s8 + 2 * u][j >> 1], sel);
+        pacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ahi),
+                                                          __builtin_bit_cast(bf16x8_t, bv), pacc[j], 0, 0, 0);
+        pacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, alo),
+                                                          __builtin_bit_cast(bf16x8_t, bv), pacc[j], 0, 0, 0);
       }
     }
   }
-  // the wave's four row residues (lanes l, l^16, l^32, l^48) hold the same columns
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int bl = 0; bl < kFastSeq; ++bl) acc[j][bl] = sum_lanes_16_32_48(acc[j][bl]);
-  if (lane < 16) {
+  // lanes 0-15 hold output rows 0..3 (the sequences) of column 8 dc + j
+  if (g4 == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int h = 0; h < kFastSeq / 4; ++h)
-        *reinterpret_cast<float4*>(&red[wave][dc][j][4 * h]) =
-            make_float4(acc[j][4 * h], acc[j][4 * h + 1], acc[j][4 * h + 2], acc[j][4 * h + 3]);
+      *reinterpret_cast<float4*>(&red[wave][dc][j][0]) = make_float4(pacc[j][0], pacc[j][1], pacc[j][2], pacc[j][3]);
   }
   __syncthreads();
   // outputs: f = (bl, d), d fastest
