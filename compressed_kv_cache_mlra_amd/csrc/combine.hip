@@ -262,7 +262,7 @@ constexpr int kFastDh = 128;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
-static_assert(kFastSeq == 4, "the product's lanes 0-15 carry four sequences");
+static_assert(kFastSeq % 4 == 0 && kFastSeq <= 16, "sequences are MFMA rows, four per lane group");
 
 template <int W, int KB, bool PB>
 __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs a) {
@@ -427,11 +427,12 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
       }
     }
   }
-  // lanes 0-15 hold output rows 0..3 (the sequences) of column 8 dc + j
-  if (g4 == 0) {
+  // lane group g4 holds output rows (sequences) 4 g4 .. 4 g4 + 3 of column 8 dc + j
+  if (g4 < kFastSeq / 4) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<float4*>(&red[wave][dc][j][0]) = make_float4(pacc[j][0], pacc[j][1], pacc[j][2], pacc[j][3]);
+      *reinterpret_cast<float4*>(&red[wave][dc][j][4 * g4]) =
+          make_float4(pacc[j][0], pacc[j][1], pacc[j][2], pacc[j][3]);
   }
   __syncthreads();
   // outputs: f = (bl, d), d fastest
