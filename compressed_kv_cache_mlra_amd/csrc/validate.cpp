@@ -32,6 +32,8 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (d->dtype == MLRA_F32 && (w % 4 != 0 || d->d_r % 4 != 0)) return MLRA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(d->max_pages_per_seq) * ps > INT32_MAX) return MLRA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(d->batch) * d->max_pages_per_seq > INT32_MAX) return MLRA_ERR_INVALID_ARG;
+  // the plan counts tiles (>= 16 tokens) of all sequences in int32
+  if (static_cast<int64_t>(d->batch) * d->max_pages_per_seq * ps / 16 > INT32_MAX) return MLRA_ERR_UNSUPPORTED;
   if (!(d->softmax_scale == d->softmax_scale) || !(d->out_scale == d->out_scale) ||
       isinf(d->softmax_scale) || isinf(d->out_scale))
     return MLRA_ERR_INVALID_ARG;

@@ -67,6 +67,7 @@ BAD_DESCS = [
     (dict(d_r=-8), mlra.ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), mlra.ERR_INVALID_ARG),
     (dict(batch=4097), mlra.ERR_UNSUPPORTED),          # the plan keeps the batch in LDS
+    (dict(batch=4096, max_pages_per_seq=1 << 18, page_size=256), mlra.ERR_UNSUPPORTED),  # int32 tile count
 ]
 
 
