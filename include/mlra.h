@@ -90,7 +90,8 @@ typedef struct {
   int32_t blocks_per_head;   /* k: blocks each head attends (divides b) */
   int32_t d_r;               /* RoPE key width (0 .. 512) */
   int32_t page_size;         /* tokens per page: power of two in [16, 256] */
-  int32_t max_pages_per_seq; /* page-table row length */
+  int32_t max_pages_per_seq; /* page-table row length (batch * max_pages_per_seq * page_size
+                                <= 16 * INT32_MAX, else MLRA_ERR_UNSUPPORTED) */
   int32_t num_pages;         /* pages in the pool */
   int32_t d_model;           /* append only: width of x */
   int32_t dtype;             /* mlra_dtype */
