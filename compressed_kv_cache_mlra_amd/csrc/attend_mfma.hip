@@ -29,6 +29,10 @@
 //    (chunk ^ (row & 7)) so both read patterns avoid LDS bank conflicts.
 //  - Page ids of the whole unit are gathered into LDS once, so the tile loop
 //    issues no scalar loads.
+//  - FP8 caches: rows enter LDS as stored (E4M3FN latent codes, then the bf16
+//    k^R), 44% fewer LDS bytes per tile than widened rows; each latent operand
+//    is an 8-byte LDS read widened to 8 bf16 values in registers (exact: every
+//    E4M3 value is a bf16 value).
 #include <type_traits>
 
 #include "common.h"
@@ -67,9 +71,10 @@ struct Cfg {
   // register set, live only before the loop); otherwise the second is
   // requested once the first is in LDS. Chosen per shape by measurement.
   static constexpr bool P2 = P2_;
-  static constexpr int ROWB = ROW * 2;  // bytes of a row in LDS (bf16 throughout)
-  static constexpr int CPR = ROW / 8;   // 16-byte LDS chunks per row
-  static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROWB;  // bytes of a row in HBM
+  static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROW * 2;  // bytes of a row in HBM
+  // bytes of a row in LDS: rows are stored as they come from HBM (FP8: the
+  // E4M3 codes, widened to bf16 when the MFMA operands are read)
+  static constexpr int ROWB = ROWG;
   static constexpr int CPRG = ROWG / 16;                     // 16-byte HBM chunks per row
   static constexpr int LATC = F8 ? NBR * W / 16 : 0;         // HBM chunks of latent codes per row
   static constexpr int TASKS = NBR * HT;
@@ -101,7 +106,7 @@ struct Cfg {
   static constexpr int PT_CAP_RAW =
       (160 * 1024 / OCC - 2 * TILE_BYTES - SEQ_WIN * 4 - NWAVES * 64 - XCH_BYTES - 256) / 4;
   static constexpr int PT_CAP = PT_CAP_RAW > 4096 ? 4096 : PT_CAP_RAW;
-  static_assert(ROW % 64 == 0, "rows must be whole 128-byte groups");
+  static_assert(ROWB % 128 == 0, "rows must be whole 128-byte groups (the LDS swizzle)");
   static_assert(W % (128 * CS) == 0 && DR % 32 == 0 && KK % CS == 0, "");
   static_assert(TT % 32 == 0 && NSUB % G == 0, "");
   static_assert(TILE_CHUNKS % NLT == 0, "");
@@ -170,6 +175,19 @@ __device__ __forceinline__ u32x4_t gload16_stream(const uint8_t* p) {
 
 __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// 8 E4M3FN codes (8 bytes of LDS) -> 8 bf16 values (exact: E4M3 values are bf16 values)
+__device__ __forceinline__ u32x4_t widen8(const uint8_t* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t c = *reinterpret_cast<const u32x2_t*>(p);
+  u32x4_t r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h], 1.0f, false));
+    r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h], 1.0f, true));
+  }
+  return r;
 }
 
 template <class C>
@@ -291,26 +309,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       const int r = p / C::CPRG, lc = p % C::CPRG;
       u32x4_t v = ring[k];
       if (r >= valid) v = u32x4_t{0u, 0u, 0u, 0u};
-      if constexpr (C::F8) {
-        if (lc < C::LATC) {
-          // 16 latent codes -> 16 bf16 values (exact: E4M3 values are bf16 values)
-          u32x4_t lo, hi;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            lo[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, false));
-            lo[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, true));
-            hi[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + h], 1.0f, false));
-            hi[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + h], 1.0f, true));
-          }
-          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * ((2 * lc) ^ (r & 7))) = lo;
-          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * ((2 * lc + 1) ^ (r & 7))) = hi;
-        } else {
-          const int chunk = C::NBR * C::W / 8 + (lc - C::LATC);  // the bf16 RoPE key, copied
-          *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (chunk ^ (r & 7))) = v;
-        }
-      } else {
-        *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (lc ^ (r & 7))) = v;
-      }
+      *reinterpret_cast<u32x4_t*>(dst + r * C::ROWB + 16 * (lc ^ (r & 7))) = v;
     }
   };
 
@@ -480,11 +479,19 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           const int kl = kb + u;
           if (kl < C::KKH) {
             const int kk = cs * C::KKH + kl;
-            const int chunk = kk < C::KKC ? blk * (C::W / 8) + 4 * kk + g4
-                                          : C::NBR * (C::W / 8) + 4 * (kk - C::KKC) + g4;
-            const int co = 16 * (chunk ^ key);
-            A0[u] = lds_read16(rp0 + co);
-            A1[u] = lds_read16(rp1 + co);
+            if (C::F8 && kk < C::KKC) {
+              // 8 latent codes of the row: half of a 16-byte chunk
+              const int ch = blk * (C::W / 16) + 2 * kk + (g4 >> 1);
+              const int co = 16 * (ch ^ key) + 8 * (g4 & 1);
+              A0[u] = widen8(rp0 + co);
+              A1[u] = widen8(rp1 + co);
+            } else {
+              const int lat = C::F8 ? C::NBR * C::W / 16 : C::NBR * (C::W / 8);  // chunks before k^R
+              const int chunk = kk < C::KKC ? blk * (C::W / 8) + 4 * kk + g4 : lat + 4 * (kk - C::KKC) + g4;
+              const int co = 16 * (chunk ^ key);
+              A0[u] = lds_read16(rp0 + co);
+              A1[u] = lds_read16(rp1 + co);
+            }
           }
         }
 #pragma unroll
@@ -516,14 +523,24 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           }
         }
       }
-      // value-side rows of the first 128-column group, read while the scores finish
-      const int vchunk0 = blk * (C::W / 8) + 16 * (cs * C::NQ) + m16;
-      u32x4_t R[8];
+      // value-side rows: 8 columns (col group 16 q' + m16 of the block, q' the
+      // 128-column group) of 8 token rows
+      auto read_rows = [&](int qg, u32x4_t* R) __attribute__((always_inline)) {
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
-        R[v] = lds_read16(sb + tr * C::ROWB + 16 * (vchunk0 ^ (tr & 7)));
-      }
+        for (int v = 0; v < 8; ++v) {
+          const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
+          if constexpr (C::F8) {
+            const int ch = blk * (C::W / 16) + 8 * qg + (m16 >> 1);
+            R[v] = widen8(sb + tr * C::ROWB + 16 * (ch ^ (tr & 7)) + 8 * (m16 & 1));
+          } else {
+            const int chunk = blk * (C::W / 8) + 16 * qg + m16;
+            R[v] = lds_read16(sb + tr * C::ROWB + 16 * (chunk ^ (tr & 7)));
+          }
+        }
+      };
+      // the first 128-column group, read while the scores finish
+      u32x4_t R[8];
+      read_rows(cs * C::NQ, R);
       if (valid < C::TT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -560,14 +577,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // ---- values: O^T[col][head] += C^T[col][tokens] P^T[tokens][head]
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) {
-        if (q > 0) {
-          const int chunk = blk * (C::W / 8) + 16 * (cs * C::NQ + q) + m16;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            const int tr = rowbase + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4));
-            R[v] = lds_read16(sb + tr * C::ROWB + 16 * (chunk ^ (tr & 7)));
-          }
-        }
+        if (q > 0) read_rows(cs * C::NQ + q, R);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
