@@ -18,7 +18,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP8_BS = 0, 1, 2, 3
 METHODS = {"MHA": 0, "MQA": 1, "GQA": 2, "MLA": 3, "MFA": 4, "TPA": 5, "MLRA": 6}
 
 
@@ -77,6 +77,10 @@ def lib():
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_block_encode.argtypes = [vp, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_float)]
+        L.oracle_fp8_block_encode.restype = None
+        L.oracle_fp8_row_bytes.argtypes = [sp]
+        L.oracle_fp8_row_bytes.restype = ctypes.c_int64
         L.oracle_cache_elems_per_token.argtypes = [ctypes.c_int32] * 7
         L.oracle_cache_elems_per_token.restype = ctypes.c_double
         L.oracle_cache_elems_per_device.argtypes = [ctypes.c_int32] * 9
@@ -95,7 +99,7 @@ def shape_of(inp, softmax_scale: Optional[float] = None, out_scale: Optional[flo
         batch=s.batch, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks,
         blocks_per_head=s.blocks_per_head, d_r=s.d_r, page_size=s.page_size,
         max_pages_per_seq=inp.max_pages_per_seq, d_model=s.d_model,
-        dtype={"bf16": BF16, "f32": F32, "fp8": FP8}[s.dtype],
+        dtype={"bf16": BF16, "f32": F32, "fp8": FP8, "fp8b": FP8_BS}[s.dtype],
         softmax_scale=s.softmax_scale if softmax_scale is None else softmax_scale,
         out_scale=s.out_scale if out_scale is None else out_scale,
         cache_scale=getattr(s, "cache_scale", 0.0), d_cq=getattr(s, "d_cq", 0),
@@ -158,11 +162,25 @@ def append(inp, pool: np.ndarray, c_out: bool = True):
     """Applies the latent append to `pool` in place; returns c_new [B][d_c]."""
     s = inp.shape
     shp = shape_of(inp)
-    c_dtype = np.float32 if s.dtype == "fp8" else pool.dtype  # fp8: the latent before encoding
+    c_dtype = np.float32 if s.dtype in ("fp8", "fp8b") else pool.dtype  # fp8: the latent before encoding
     c = np.zeros((s.batch, s.d_c), dtype=c_dtype) if c_out else None
     lib().oracle_append(ctypes.byref(shp), _ptr(pool), _iptr(inp.page_table), _iptr(inp.positions),
                         _ptr(inp.x), _ptr(inp.w_dkv), _ptr(inp.kr_new), _ptr(c))
     return c
+
+
+def fp8_block_encode(c: np.ndarray):
+    """Block-scaled E4M3FN encoding of one block of fp32 latent values:
+    returns (codes uint8 [n], scale float32)."""
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    codes = np.zeros(c.size, dtype=np.uint8)
+    sc = ctypes.c_float(0.0)
+    lib().oracle_fp8_block_encode(_ptr(c), c.size, _ptr(codes), ctypes.byref(sc))
+    return codes, np.float32(sc.value)
+
+
+def fp8_row_bytes(inp) -> int:
+    return int(lib().oracle_fp8_row_bytes(ctypes.byref(shape_of(inp))))
 
 
 def block_of(inp, head: int, jj: int) -> int:

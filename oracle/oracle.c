@@ -37,6 +37,7 @@
  */
 #include "oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -100,19 +101,45 @@ uint8_t oracle_e4m3_encode(float x) {
   return sgn | (uint8_t)((E + 6) * 8 + (int)n);
 }
 
+static int is_fp8(const oracle_shape* s) {
+  return s->dtype == ORACLE_FP8_E4M3 || s->dtype == ORACLE_FP8_E4M3_BS;
+}
+
+int64_t oracle_fp8_row_bytes(const oracle_shape* s) {
+  int64_t rb = s->d_c + 2 * (int64_t)s->d_r;
+  if (s->dtype == ORACLE_FP8_E4M3_BS) rb += 4 * (int64_t)s->n_blocks;
+  return (rb + 15) / 16 * 16;
+}
+
+void oracle_fp8_block_encode(const float* c, int32_t n, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int32_t i = 0; i < n; ++i)
+    if (fabsf(c[i]) > amax) amax = fabsf(c[i]); /* false for NaN */
+  float sc = amax / 448.0f;
+  if (!(sc >= FLT_MIN) || isinf(sc)) sc = 1.0f;
+  const float inv = 1.0f / sc;
+  for (int32_t i = 0; i < n; ++i) codes[i] = oracle_e4m3_encode(c[i] * inv);
+  *scale = sc;
+}
+
 /* Latent value `col` and RoPE value `r` of pool row `row_idx`. */
 static double pool_latent(const oracle_shape* s, const void* pool, int64_t row_idx, int32_t col) {
-  if (s->dtype == ORACLE_FP8_E4M3) {
-    const int64_t rb = s->d_c + 2 * (int64_t)s->d_r;
-    const double cs = s->cache_scale > 0 ? s->cache_scale : 1.0;
-    return oracle_e4m3_decode(((const uint8_t*)pool)[row_idx * rb + col]) * cs;
+  if (is_fp8(s)) {
+    const uint8_t* row = (const uint8_t*)pool + row_idx * oracle_fp8_row_bytes(s);
+    double sc = s->cache_scale > 0 ? s->cache_scale : 1.0;
+    if (s->dtype == ORACLE_FP8_E4M3_BS) {
+      float f; /* the scale of col's block in this row */
+      memcpy(&f, row + s->d_c + 2 * (int64_t)s->d_r + 4 * (int64_t)(col / (s->d_c / s->n_blocks)), 4);
+      sc = f;
+    }
+    return oracle_e4m3_decode(row[col]) * sc;
   }
   return elem(s->dtype, pool, row_idx * (s->d_c + s->d_r) + col);
 }
 
 static double pool_rope(const oracle_shape* s, const void* pool, int64_t row_idx, int32_t r) {
-  if (s->dtype == ORACLE_FP8_E4M3) {
-    const int64_t rb = s->d_c + 2 * (int64_t)s->d_r;
+  if (is_fp8(s)) {
+    const int64_t rb = oracle_fp8_row_bytes(s);
     uint16_t v;
     memcpy(&v, (const uint8_t*)pool + row_idx * rb + s->d_c + 2 * (int64_t)r, 2);
     return elem(ORACLE_BF16, &v, 0);
@@ -122,7 +149,7 @@ static double pool_rope(const oracle_shape* s, const void* pool, int64_t row_idx
 
 /* Encoding of the non-cache arrays (queries, weights, x, k^R_new). */
 static int32_t arrays_dtype(const oracle_shape* s) {
-  return s->dtype == ORACLE_FP8_E4M3 ? ORACLE_BF16 : s->dtype;
+  return is_fp8(s) ? ORACLE_BF16 : s->dtype;
 }
 
 static void store_elem(int32_t dtype, void* base, int64_t idx, double v) {
@@ -296,21 +323,33 @@ void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
                    const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
                    void* c_out) {
   const int32_t DC = s->d_c, DR = s->d_r, DM = s->d_model, ROW = s->d_c + s->d_r;
-  if (s->dtype == ORACLE_FP8_E4M3) {
-    const int64_t rb = DC + 2 * (int64_t)DR;
+  if (is_fp8(s)) {
+    const int64_t rb = oracle_fp8_row_bytes(s);
     const float inv = 1.0f / (float)(s->cache_scale > 0 ? s->cache_scale : 1.0);
+    float* cf = (float*)malloc(sizeof(float) * (size_t)(DC > 0 ? DC : 1));
     for (int32_t b = 0; b < s->batch; ++b) {
       uint8_t* row = (uint8_t*)pool + oracle_row_index(s, page_table, b, positions[b]) * rb;
       for (int32_t cc = 0; cc < DC; ++cc) {
         double v = 0.0;
         for (int32_t m = 0; m < DM; ++m)
           v += elem(ORACLE_BF16, x, (int64_t)b * DM + m) * elem(ORACLE_BF16, w_dkv, (int64_t)m * DC + cc);
-        const float cf = (float)v;
-        row[cc] = oracle_e4m3_encode(cf * inv);
-        if (c_out) ((float*)c_out)[(int64_t)b * DC + cc] = cf;
+        cf[cc] = (float)v;
+        if (c_out) ((float*)c_out)[(int64_t)b * DC + cc] = cf[cc];
+      }
+      if (s->dtype == ORACLE_FP8_E4M3_BS) {
+        const int32_t W = DC / s->n_blocks;
+        memset(row, 0, (size_t)rb); /* the pad bytes */
+        for (int32_t j = 0; j < s->n_blocks; ++j) {
+          float sc;
+          oracle_fp8_block_encode(cf + (int64_t)j * W, W, row + (int64_t)j * W, &sc);
+          memcpy(row + DC + 2 * (int64_t)DR + 4 * (int64_t)j, &sc, 4);
+        }
+      } else {
+        for (int32_t cc = 0; cc < DC; ++cc) row[cc] = oracle_e4m3_encode(cf[cc] * inv);
       }
       memcpy(row + DC, (const uint16_t*)kr_new + (int64_t)b * DR, 2 * (size_t)DR);
     }
+    free(cf);
     return;
   }
   const int32_t dt = s->dtype;

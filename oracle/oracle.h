@@ -24,8 +24,13 @@ extern "C" {
  * selects a quantised cache (the FP8 latent quantisation the lesty.tech MLA
  * explainer mentions in section 5): cache rows hold the latent as OCP FP8
  * E4M3FN codes followed by the RoPE key in bf16, every latent value being
- * (decoded code) x cache_scale; all other arrays are then bf16. */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
+ * (decoded code) x cache_scale; all other arrays are then bf16.
+ * ORACLE_FP8_E4M3_BS is the same cache with one fp32 scale per token and
+ * latent block instead of cache_scale: a row is the d_c codes, the d_r bf16
+ * RoPE values, n_blocks fp32 scales, then zero bytes up to a multiple of 16
+ * (oracle_fp8_row_bytes), and latent value (row, col) = decoded code x the
+ * scale of col's block in that row. */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2, ORACLE_FP8_E4M3_BS = 3 };
 
 /* Problem shape, in the notation of the MLRA paper page (Table 6 notation):
  * h query heads of width d_h; a latent of width d_c cut into n_blocks blocks of
@@ -42,7 +47,7 @@ typedef struct {
   int32_t page_size;
   int32_t max_pages_per_seq;
   int32_t d_model;         /* append only */
-  int32_t dtype;           /* ORACLE_F32 or ORACLE_BF16, for every input array */
+  int32_t dtype;           /* ORACLE_F32, ORACLE_BF16 (every input array) or an FP8 cache */
   double softmax_scale;    /* <= 0 selects 1 / sqrt(d_h + d_r) */
   double out_scale;        /* <= 0 selects 1 / sqrt(blocks_per_head) */
   double cache_scale;      /* FP8 caches: scale of every latent code (<= 0 selects 1) */
@@ -86,6 +91,8 @@ void oracle_decode_absorbed(const oracle_shape* s, const void* pool, const int32
  * row of token positions[b]; c_out (nullable) receives the rounded latent.
  * FP8 caches: c is rounded to fp32, multiplied in fp32 by the fp32 reciprocal
  * of cache_scale and encoded; c_out then receives the fp32 c (before encoding).
+ * Block-scaled FP8 caches: c is rounded to fp32 and every latent block of the
+ * row is encoded with oracle_fp8_block_encode (its own scale).
  *   x: [batch][d_model], w_dkv: [d_model][d_c], kr_new: [batch][d_r] */
 void oracle_append(const oracle_shape* s, void* pool, const int32_t* page_table,
                    const int32_t* positions, const void* x, const void* w_dkv, const void* kr_new,
@@ -121,6 +128,18 @@ uint16_t oracle_round_bf16(double v);
  * above saturate to 448, NaN gives 0x7F. */
 double oracle_e4m3_decode(uint8_t code);
 uint8_t oracle_e4m3_encode(float x);
+
+/* Bytes of one cache row of an FP8 cache: d_c + 2 d_r, plus for the
+ * block-scaled layout 4 n_blocks, rounded up to a multiple of 16. */
+int64_t oracle_fp8_row_bytes(const oracle_shape* s);
+
+/* Block-scaled encoding of n fp32 latent values (one block of one token): the
+ * block's scale is its largest magnitude divided by 448 in fp32 (so that value
+ * gets the largest code), or 1 where that quotient is 0, below the smallest
+ * normal fp32 or not finite; each code is oracle_e4m3_encode(c[i] x (1 / scale)),
+ * the reciprocal and the product rounded to fp32. NaN values are skipped in
+ * the largest magnitude (and encode to 0x7F). */
+void oracle_fp8_block_encode(const float* c, int32_t n, uint8_t* codes, float* scale);
 
 /* KV-cache elements loaded per token per device (Table 1 of the MLRA paper
  * page), for the methods listed there plus MLRA's block split.

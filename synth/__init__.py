@@ -28,6 +28,12 @@ uniform in 0..7: magnitudes between 1/16 and 1.875, RMS about 0.8 like the
 N(0, 1) latents of the bf16 workloads; no zeros or NaN) and the RoPE
 key N(0, 1) in bf16; every other array is bf16. The NaN canary is code 0x7F and
 the bf16 NaN.
+
+Block-scaled FP8 caches (dtype "fp8b"): each row further holds one fp32 scale
+per latent block after the RoPE key, then zero bytes up to a multiple of 16.
+Step 3 draws the codes and RoPE key as for "fp8", then each scale as
+2^u, u uniform in [-3, 1) (fp32), so scales differ by up to 16x between tokens
+and blocks. Canary rows hold NaN scales.
 """
 from __future__ import annotations
 
@@ -49,7 +55,8 @@ class Shape:
     d_c: int
     n_blocks: int
     d_r: int
-    dtype: str  # "f32", "bf16" or "fp8" (E4M3FN latent codes, bf16 everything else)
+    dtype: str  # "f32", "bf16", "fp8" (E4M3FN latent codes, bf16 everything else) or
+    # "fp8b" (as fp8, plus an fp32 scale per token and latent block in each row)
     page_size: int = 64
     blocks_per_head: int = 1
     d_model: int = 0
@@ -72,12 +79,18 @@ class Shape:
     def row_bytes(self) -> int:
         if self.dtype == "fp8":
             return self.d_c + 2 * self.d_r
+        if self.dtype == "fp8b":
+            return (self.d_c + 2 * self.d_r + 4 * self.n_blocks + 15) // 16 * 16
         return self.row * (2 if self.dtype == "bf16" else 4)
+
+    @property
+    def is_fp8(self) -> bool:
+        return self.dtype in ("fp8", "fp8b")
 
     @property
     def arrays_dtype(self) -> str:
         """Encoding of queries, weights and append inputs."""
-        return "bf16" if self.dtype == "fp8" else self.dtype
+        return "bf16" if self.is_fp8 else self.dtype
 
     @property
     def heads_per_block(self) -> int:
@@ -183,10 +196,23 @@ def _fp8_pool(rng: np.random.Generator, pages_rows, d_c: int, d_r: int) -> np.nd
     return pool
 
 
-def _FP8_NAN_ROW(d_c: int, d_r: int) -> np.ndarray:
-    row = np.empty(d_c + 2 * d_r, dtype=np.uint8)
+def _fp8b_pool(rng: np.random.Generator, pages_rows, shape: "Shape") -> np.ndarray:
+    """Block-scaled FP8 rows: the fp8 row, n_blocks fp32 scales 2^u, zero pad."""
+    d_c, d_r, nb = shape.d_c, shape.d_r, shape.n_blocks
+    base = _fp8_pool(rng, pages_rows, d_c, d_r)
+    u = rng.uniform(-3.0, 1.0, size=tuple(pages_rows) + (nb,))
+    scales = np.exp2(u).astype(np.float32)
+    pool = np.zeros(tuple(pages_rows) + (shape.row_bytes,), dtype=np.uint8)
+    pool[..., :d_c + 2 * d_r] = base
+    pool[..., d_c + 2 * d_r:d_c + 2 * d_r + 4 * nb] = scales.view(np.uint8).reshape(tuple(pages_rows) + (4 * nb,))
+    return pool
+
+
+def _FP8_NAN_ROW(d_c: int, d_r: int, row_bytes: int = 0, n_scales: int = 0) -> np.ndarray:
+    row = np.zeros(max(row_bytes, d_c + 2 * d_r), dtype=np.uint8)
     row[:d_c] = 0x7F
-    row[d_c:] = np.full(d_r, BF16_NAN, dtype=np.uint16).view(np.uint8)
+    row[d_c:d_c + 2 * d_r] = np.full(d_r, BF16_NAN, dtype=np.uint16).view(np.uint8)
+    row[d_c + 2 * d_r:d_c + 2 * d_r + 4 * n_scales] = np.full(n_scales, F32_NAN, dtype=np.float32).view(np.uint8)
     return row
 
 
@@ -250,6 +276,9 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
         if shape.dtype == "fp8":
             pool = _fp8_pool(rng, (n_pages, P), shape.d_c, shape.d_r)
             nanv = _FP8_NAN_ROW(shape.d_c, shape.d_r)
+        elif shape.dtype == "fp8b":
+            pool = _fp8b_pool(rng, (n_pages, P), shape)
+            nanv = _FP8_NAN_ROW(shape.d_c, shape.d_r, shape.row_bytes, shape.n_blocks)
         else:
             pool = _normal(rng, (n_pages, P, row), 1.0, shape.dtype)
             nanv = BF16_NAN if shape.dtype == "bf16" else F32_NAN

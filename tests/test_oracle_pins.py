@@ -580,6 +580,141 @@ def test_fp8_append_encodes_the_fp32_latent():
     assert np.array_equal(pool[~changed], inp.pool[~changed])
 
 
+def _fp8b_dequantised(inp):
+    """The block-scaled pool's rows as float64 [pages][P][d_c + d_r]: codes
+    decoded by the library's E4M3FN type times the row's per-block fp32 scale
+    (read as raw float32 bytes), the RoPE key from its bf16 bits."""
+    torch = pytest.importorskip("torch")
+    s = inp.shape
+    pool = inp.pool
+    codes = torch.from_numpy(np.ascontiguousarray(pool[..., :s.d_c])).view(torch.float8_e4m3fn).double().numpy()
+    o = s.d_c + 2 * s.d_r
+    scales = np.ascontiguousarray(pool[..., o:o + 4 * s.n_blocks]).view(np.float32).astype(np.float64)
+    lat = codes * np.repeat(scales, s.w, axis=-1)
+    rope = synth.bf16_bits_to_f32(np.ascontiguousarray(pool[..., s.d_c:o]).view(np.uint16)).astype(np.float64)
+    return np.concatenate([lat, rope], axis=-1)
+
+
+def test_fp8b_row_layout():
+    """Block-scaled rows: codes, bf16 RoPE key, one fp32 scale per block, zero
+    pad to a multiple of 16 bytes."""
+    for d_c, d_r, nb, want in ((512, 64, 4, 656), (512, 64, 1, 656), (128, 64, 1, 272), (512, 64, 2, 656),
+                               (64, 16, 4, 112)):
+        s = synth.Shape(batch=1, n_heads=8, d_h=16, d_c=d_c, n_blocks=nb, d_r=d_r, dtype="fp8b")
+        assert s.row_bytes == want
+        inp = synth.make_inputs(s, ("list", [20]), 1)
+        assert oracle.fp8_row_bytes(inp) == want
+        assert inp.pool.shape[-1] == want
+        assert np.all(inp.pool[..., d_c + 2 * d_r + 4 * nb:] == 0)
+
+
+def test_fp8b_cache_equals_textbook_on_dequantised_rows():
+    """A block-scaled FP8 cache reads latent (row, col) as decoded code x the
+    scale of col's block in that row: the oracle equals textbook attention over
+    the dequantised rows, on every (sequence, head) pair, blocks_per_head 1 and 2."""
+    for k in (1, 2):
+        inp = _small("fp8b", lengths=("list", [130, 1, 77]), batch=3, k=k, seed=40 + k)
+        rows = _fp8b_dequantised(inp)
+        o, l = oracle.decode_unabsorbed(inp)
+        twin = synth.make_inputs(inp.shape, ("list", [130, 1, 77]), 40 + k)
+        twin.pool = np.ascontiguousarray(rows)
+        for b in range(3):
+            for i in range(inp.shape.n_heads):
+                ref, rl = _textbook(twin, b, i)
+                r = b * inp.shape.n_heads + i
+                assert np.abs(o[r] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), (k, b, i)
+                assert np.abs(l[r] - rl).max() <= 1e-12 * max(1.0, np.abs(rl).max())
+        a, _ = oracle.decode_absorbed(inp)
+        assert np.abs(a - o).max() <= 1e-12 * np.abs(o).max()
+
+
+def test_fp8b_equal_scales_equal_per_cache_scale():
+    """Every block scale set to 0.5 reads exactly like the per-cache-scaled
+    FP8 cache of the same codes with cache_scale 0.5."""
+    kw = dict(batch=3, n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16)
+    sb = synth.Shape(dtype="fp8b", **kw)
+    inp_b = synth.make_inputs(sb, ("list", [150, 1, 70]), 23)
+    o = kw["d_c"] + 2 * kw["d_r"]
+    sc = inp_b.pool[..., o:o + 16].view(np.float32)
+    finite = np.isfinite(sc)
+    sc[finite] = 0.5  # canary rows keep their NaN scales
+    s8 = synth.Shape(dtype="fp8", cache_scale=0.5, **kw)
+    inp8 = synth.make_inputs(s8, ("list", [150, 1, 70]), 23)
+    inp8.pool = np.ascontiguousarray(inp_b.pool[..., :o])
+    for f in ("page_table", "seq_lens", "q_c", "q_r", "w_uk", "w_uv", "max_pages_per_seq"):
+        setattr(inp8, f, getattr(inp_b, f))
+    ob, lb = oracle.decode_unabsorbed(inp_b)
+    o8, l8 = oracle.decode_unabsorbed(inp8)
+    assert np.all(np.isfinite(ob))
+    assert np.array_equal(ob, o8) and np.array_equal(lb, l8)
+
+
+def test_fp8b_block_encode_closed_forms():
+    torch = pytest.importorskip("torch")
+    # the largest magnitude gets the largest code; scale = amax / 448 in fp32
+    codes, sc = oracle.fp8_block_encode(np.array([1.0, -2.0, 0.25, 0.0], np.float32))
+    assert sc == np.float32(2.0) / np.float32(448.0)
+    assert codes[1] == 0xFE and oracle.e4m3_decode(int(codes[0])) * float(sc) == pytest.approx(1.0, rel=2 ** -4)
+    assert codes[3] == 0x00
+    # all zero: scale 1, zero codes; a NaN is skipped and encodes to 0x7F
+    codes, sc = oracle.fp8_block_encode(np.zeros(8, np.float32))
+    assert sc == 1.0 and np.all(codes == 0)
+    codes, sc = oracle.fp8_block_encode(np.array([np.nan, 3.5, -7.0], np.float32))
+    assert sc == np.float32(7.0) / np.float32(448.0) and codes[0] == 0x7F and codes[2] == 0xFE
+    # an infinite value: scale 1, the values saturate
+    codes, sc = oracle.fp8_block_encode(np.array([np.inf, 1.0], np.float32))
+    assert sc == 1.0 and codes[0] == 0x7E and codes[1] == 0x38
+    # a block too small for a normal scale: scale 1
+    codes, sc = oracle.fp8_block_encode(np.array([1e-39, -2e-39], np.float32))
+    assert sc == 1.0
+    # random blocks: codes = the library's E4M3 rounding of c x fp32(1 / scale);
+    # the decoded value is within half a code spacing of c (relative 2^-4 above
+    # the subnormal range)
+    rng = np.random.default_rng(9)
+    for mag in (1e-3, 1.0, 1e4):
+        c = (rng.standard_normal(128) * mag).astype(np.float32)
+        codes, sc = oracle.fp8_block_encode(c)
+        amax = np.float32(np.abs(c).max())
+        assert sc == amax / np.float32(448.0)
+        inv = np.float32(1.0) / sc
+        want = torch.from_numpy(c * inv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, want)
+        dec = np.array([oracle.e4m3_decode(int(v)) for v in codes]) * float(sc)
+        err = np.abs(dec - c.astype(np.float64))
+        bound = np.maximum(2.0 ** -4 * np.abs(c), 2.0 ** -10 * float(sc)) * (1 + 1e-6)
+        assert np.all(err <= bound)
+
+
+def test_fp8b_append_encodes_each_block_with_its_own_scale():
+    """Block-scaled append: c = x W^DKV (numpy float64 matmul) rounded to
+    fp32; each block's scale is its fp32 largest magnitude / 448 and its codes
+    the library's E4M3 rounding of c x fp32(1 / scale); the RoPE key lands as
+    bf16, the pad bytes are zero, and nothing else moves."""
+    torch = pytest.importorskip("torch")
+    s = synth.Shape(batch=3, n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16, dtype="fp8b", d_model=96)
+    inp = synth.make_inputs(s, ("list_append", [0, 63, 200]), 8)
+    pool = inp.pool.copy()
+    c = oracle.append(inp, pool)
+    c_ref = (_f(inp.x) @ _f(inp.w_dkv)).astype(np.float32)
+    assert np.all(np.abs(c - c_ref) <= 2 * np.spacing(np.abs(c_ref)))
+    o = s.d_c + 2 * s.d_r
+    changed = np.zeros(pool.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // s.page_size], pos % s.page_size
+        changed[pg, off] = True
+        row = pool[pg, off]
+        for j in range(s.n_blocks):
+            blk = c[b, j * s.w:(j + 1) * s.w]
+            sc = np.float32(np.abs(blk).max()) / np.float32(448.0)
+            assert row[o + 4 * j:o + 4 * j + 4].view(np.float32)[0] == sc
+            want = torch.from_numpy(blk * (np.float32(1.0) / sc)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(row[j * s.w:(j + 1) * s.w], want)
+        assert np.array_equal(row[s.d_c:o].view(np.uint16), inp.kr_new[b])
+        assert np.all(row[o + 4 * s.n_blocks:] == 0)
+    assert np.array_equal(pool[~changed], inp.pool[~changed])
+
+
 # ------------------------------------------------- RoPE and the query path
 # lesty.tech section 4: k^R = RoPE(h W^KR), the query split the same way; the
 # rotation is RoFormer's (cited by the MLRA index page). Readings in the design notes.
