@@ -39,7 +39,8 @@ METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8
 KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
 # rocprofv3 counter summaries of the attention kernel, per workload
 PROFILE_TAGS = {2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
-                5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k", 7: "mlra4_b32_ctx8k_layer"}
+                5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k", 7: "mlra4_b32_ctx8k_layer",
+                8: "mlra4_fp8_block_scaled_b32_ctx8k"}
 
 
 def _counters_file(workload: int) -> str:
@@ -53,7 +54,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")

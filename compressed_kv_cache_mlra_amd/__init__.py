@@ -21,10 +21,10 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmlra.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP8_E4M3_BS = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class MlraError(RuntimeError):
@@ -49,7 +49,7 @@ def make_desc(batch, n_heads, d_h, d_c, n_blocks, d_r, max_pages_per_seq, num_pa
               page_size=64, blocks_per_head=1, d_model=0, softmax_scale=0.0, out_scale=0.0,
               cache_scale=0.0, d_cq=0, rope_base=0.0) -> MlraDesc:
     if isinstance(dtype, str):
-        dtype = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}[dtype]
+        dtype = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8b": FP8_E4M3_BS}[dtype]
     return MlraDesc(batch=batch, n_heads=n_heads, d_h=d_h, d_c=d_c, n_blocks=n_blocks,
                     blocks_per_head=blocks_per_head, d_r=d_r, page_size=page_size,
                     max_pages_per_seq=max_pages_per_seq, num_pages=num_pages, d_model=d_model,
@@ -172,10 +172,17 @@ def _row(desc):
 
 def _pool_ptr(pool, desc):
     """The cache pool: elements of desc.dtype, or bytes for FP8 caches."""
-    if desc.dtype == FP8_E4M3:
+    if desc.dtype in (FP8_E4M3, FP8_E4M3_BS):
         return _ptr(pool, kind="bytes", name="pool",
-                    numel=desc.num_pages * desc.page_size * (desc.d_c + 2 * desc.d_r) // pool.element_size())
+                    numel=desc.num_pages * desc.page_size * fp8_row_bytes(desc) // pool.element_size())
     return _ptr(pool, desc, name="pool", numel=desc.num_pages * desc.page_size * _row(desc))
+
+
+def fp8_row_bytes(desc):
+    """Bytes of one FP8 cache row: codes, bf16 k^R, (block-scaled) one fp32
+    scale per block, rounded up to a multiple of 16."""
+    rb = desc.d_c + 2 * desc.d_r + (4 * desc.n_blocks if desc.dtype == FP8_E4M3_BS else 0)
+    return (rb + 15) // 16 * 16
 
 
 def _w(desc):
@@ -199,7 +206,7 @@ def append_latent(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out, wo
 
 def _c_out_ptr(c_out, desc):
     """c_out: fp32 for FP8 caches (the latent before encoding), else the element type; optional."""
-    if desc.dtype == FP8_E4M3:
+    if desc.dtype in (FP8_E4M3, FP8_E4M3_BS):
         return _ptr(c_out, kind="f32", name="c_out", numel=desc.batch * desc.d_c, nullable=True)
     return _ptr(c_out, desc, name="c_out", numel=desc.batch * desc.d_c, nullable=True)
 

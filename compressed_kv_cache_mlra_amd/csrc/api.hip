@@ -39,7 +39,7 @@ int make_plan(const mlra_desc* d, Plan* p) {
   int st = check_desc(d, &p->s);
   if (st != MLRA_OK) return st;
   const ShapeInfo& s = p->s;
-  const bool fp8 = d->dtype == MLRA_FP8_E4M3;
+  const int fp8 = fp8_mode(d);
   p->variant = d->dtype != MLRA_F32 ? find_mfma_variant(s.w, d->d_r, d->n_blocks, s.head_tiles, fp8)
                                     : nullptr;
   if (fp8 && !p->variant) return MLRA_ERR_UNSUPPORTED;  // FP8 caches run on the MFMA variants only
@@ -169,7 +169,7 @@ CombineArgs combine_args(const mlra_desc* d, const Plan& p, const void* ws, cons
 int hip_status(hipError_t e) { return e == hipSuccess ? MLRA_OK : MLRA_ERR_HIP; }
 
 // Element type of queries, weights and append inputs (bf16 for FP8 caches).
-int arrays_dtype(const mlra_desc* d) { return d->dtype == MLRA_FP8_E4M3 ? MLRA_BF16 : d->dtype; }
+int arrays_dtype(const mlra_desc* d) { return fp8_mode(d) ? MLRA_BF16 : d->dtype; }
 
 }  // namespace
 }  // namespace mlra
@@ -178,7 +178,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 6; }
+int mlra_abi_version(void) { return 7; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -286,6 +286,7 @@ int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_ta
   st = append_latent_mfma(desc, pool, page_table, positions, x, w_dkv, kr_new, c_out, workspace, ws_bytes, stream);
   if (st != kNotEligible) return st;
   if (!workspace) return MLRA_ERR_INVALID_ARG;  // the same contract on every path
+  if (fp8_mode(desc) == 2) return MLRA_ERR_UNSUPPORTED;  // block scales: the MFMA product only
   AppendArgs a;
   memset(&a, 0, sizeof(a));
   a.pool = pool;
@@ -299,7 +300,7 @@ int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_ta
   a.d_c = desc->d_c;
   a.d_r = desc->d_r;
   a.d_model = desc->d_model;
-  a.row = desc->dtype == MLRA_FP8_E4M3 ? desc->d_c + 2 * desc->d_r : desc->d_c + desc->d_r;
+  a.row = fp8_mode(desc) ? fp8_row_bytes(desc) : desc->d_c + desc->d_r;
   a.page_size = desc->page_size;
   a.max_pages = desc->max_pages_per_seq;
   a.num_pages = desc->num_pages;

@@ -47,7 +47,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false, bool CF_ = false,
-          int CS_ = 1, bool P2_ = false>
+          int CS_ = 1, bool P2_ = false, bool TS_ = false>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -71,10 +71,15 @@ struct Cfg {
   // register set, live only before the loop); otherwise the second is
   // requested once the first is in LDS. Chosen per shape by measurement.
   static constexpr bool P2 = P2_;
-  static constexpr int ROWG = F8 ? NBR * W + 2 * DR : ROW * 2;  // bytes of a row in HBM
+  // TS (FP8 only): every row also holds one fp32 scale per latent block after
+  // the RoPE key (at byte SCO), then zero bytes up to a multiple of 16
+  static constexpr bool TS = TS_;
+  static constexpr int SCO = NBR * W + 2 * DR;
+  static constexpr int ROWG = F8 ? (SCO + (TS ? 4 * NBR : 0) + 15) / 16 * 16 : ROW * 2;  // bytes of a row in HBM
   // bytes of a row in LDS: rows are stored as they come from HBM (FP8: the
-  // E4M3 codes, widened to bf16 when the MFMA operands are read)
-  static constexpr int ROWB = ROWG;
+  // E4M3 codes, widened to bf16 when the MFMA operands are read), padded to
+  // whole 128-byte groups for the swizzle
+  static constexpr int ROWB = (ROWG + 127) / 128 * 128;
   static constexpr int CPRG = ROWG / 16;                     // 16-byte HBM chunks per row
   static constexpr int LATC = F8 ? NBR * W / 16 : 0;         // HBM chunks of latent codes per row
   static constexpr int TASKS = NBR * HT;
@@ -86,14 +91,16 @@ struct Cfg {
   static constexpr int TILE_BYTES = TT * ROWB;
   static constexpr int TILE_CHUNKS = TT * CPRG;  // HBM chunks of one tile
   // Loader threads: the largest multiple of 64 not above NTHREADS that divides
-  // the tile's chunk count, so every loader moves the same number of chunks.
+  // the tile's chunk count, so every loader moves the same number of chunks;
+  // all threads, the last round partly idle (TAIL), where none divides it.
   static constexpr int loaders() {
     for (int n = NTHREADS; n >= 64; n -= 64)
       if (TILE_CHUNKS % n == 0) return n;
-    return 64;
+    return NTHREADS;
   }
   static constexpr int NLT = loaders();
-  static constexpr int NL = TILE_CHUNKS / NLT;  // 16-byte chunks per loader per tile
+  static constexpr bool TAIL = TILE_CHUNKS % NLT != 0;
+  static constexpr int NL = (TILE_CHUNKS + NLT - 1) / NLT;  // 16-byte chunks per loader per tile
   static constexpr int KK = (W + DR) / 32;       // score k-steps
   static constexpr int KKC = W / 32;             // k-steps over the latent part
   static constexpr int KKH = KK / CS;            // score k-steps of one wave
@@ -109,7 +116,7 @@ struct Cfg {
   static_assert(ROWB % 128 == 0, "rows must be whole 128-byte groups (the LDS swizzle)");
   static_assert(W % (128 * CS) == 0 && DR % 32 == 0 && KK % CS == 0, "");
   static_assert(TT % 32 == 0 && NSUB % G == 0, "");
-  static_assert(TILE_CHUNKS % NLT == 0, "");
+  static_assert(!TS || (F8 && NBR <= 4 && CS == 1 && SCO % 16 == 0), "token scales: one chunk, no splits");
   static_assert(PT_CAP >= 64, "LDS: room for the page-id table");
   static_assert(NTHREADS <= 1024, "");
 };
@@ -280,6 +287,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // 32-bit offset from the uniform base (scalar base + vector offset)
 #pragma unroll
       for (int k = 0; k < C::NL; ++k) {
+        if (C::TAIL && k * C::NLT + tid >= C::TILE_CHUNKS) break;
         const uint32_t off = 16u * static_cast<uint32_t>(k * C::NLT + tid);
         ring[k] = gload16_stream(base + off);
       }
@@ -291,6 +299,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 #pragma unroll
       for (int k = 0; k < C::NL; ++k) {
         const int p = k * C::NLT + tid;
+        if (C::TAIL && p >= C::TILE_CHUNKS) break;
         const int r = p / C::CPRG, lc = p % C::CPRG;
         const int j = r >> a.log2_page;
         int32_t phys = ph[0];
@@ -306,6 +315,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 #pragma unroll
     for (int k = 0; k < C::NL; ++k) {
       const int p = k * C::NLT + tid;
+      if (C::TAIL && p >= C::TILE_CHUNKS) break;
       const int r = p / C::CPRG, lc = p % C::CPRG;
       u32x4_t v = ring[k];
       if (r >= valid) v = u32x4_t{0u, 0u, 0u, 0u};
@@ -470,6 +480,17 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       const uint8_t* rp1 = rp0 + 16 * C::ROWB;
       const int key = m16 & 7;
       floatx4_t S0 = floatx4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+      // TS: the scales of this wave's block for its eight tokens (rows past
+      // the sequence end were stored as zeros)
+      float sc0[4], sc1[4];
+      if constexpr (C::TS) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t0 = rowbase + 4 * g4 + i, t1 = t0 + 16;
+          sc0[i] = *reinterpret_cast<const float*>(sb + t0 * C::ROWB + 16 * ((C::SCO / 16) ^ (t0 & 7)) + 4 * blk);
+          sc1[i] = *reinterpret_cast<const float*>(sb + t1 * C::ROWB + 16 * ((C::SCO / 16) ^ (t1 & 7)) + 4 * blk);
+        }
+      }
       constexpr int KB = 3;  // score k-steps whose operands are read ahead together
 #pragma unroll
       for (int kb = 0; kb < C::KKH; kb += KB) {
@@ -500,6 +521,17 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           if (kl < C::KKH) {
             S0 = mfma32(__builtin_bit_cast(bf16x8_t, A0[u]), Qb[kl], S0);
             S1 = mfma32(__builtin_bit_cast(bf16x8_t, A1[u]), Qb[kl], S1);
+            if constexpr (C::TS) {
+              if (kl == C::KKC - 1) {
+                // the latent part is complete: scale it per token before the
+                // RoPE k-steps add theirs
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  S0[i] *= sc0[i];
+                  S1[i] *= sc1[i];
+                }
+              }
+            }
           }
         }
       }
@@ -570,6 +602,15 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
           for (int e = 0; e < 8; ++e) O[q][e] *= scale;
+      }
+      if constexpr (C::TS) {
+        // value side: sum_t p_t (s_t code_t) = sum_t (p_t s_t) code_t; the
+        // softmax sum above keeps the unscaled p_t
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p0[i] *= sc0[i];
+          p1[i] *= sc1[i];
+        }
       }
       const u32x4_t pbu = u32x4_t{pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
                                   pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
@@ -666,10 +707,10 @@ struct Entry {
 };
 
 template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1,
-          bool P2 = false>
+          bool P2 = false, bool TS = false>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2>;
-  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? 1 : 0, C::NTHREADS, 2 * C::TILE_BYTES},
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2, TS>;
+  return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? (TS ? 2 : 1) : 0, C::NTHREADS, 2 * C::TILE_BYTES},
                &run_variant<C>};
 }
 
@@ -701,14 +742,19 @@ const Entry kVariants[] = {
     entry<512, 64, 1, 4, 1, 32, 1, true>(),
     entry<128, 64, 1, 1, 1, 32, 4, true, true>(),
     entry<256, 64, 2, 2, 1, 32, 2, true, true>(),
+    // FP8 with one scale per token and latent block (the same tunings)
+    entry<128, 64, 4, 1, 1, 32, 2, true, true, 1, true, true>(),
+    entry<512, 64, 1, 4, 1, 32, 1, true, false, 1, false, true>(),
+    entry<128, 64, 1, 1, 1, 32, 4, true, true, 1, false, true>(),
+    entry<256, 64, 2, 2, 1, 32, 2, true, true, 1, false, true>(),
 };
 
 }  // namespace
 
-const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles, bool fp8) {
+const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles, int fp8) {
   for (const Entry& e : kVariants)
     if (e.v.w == w && e.v.d_r == d_r && e.v.n_blocks == n_blocks && e.v.head_tiles == head_tiles &&
-        e.v.fp8 == (fp8 ? 1 : 0))
+        e.v.fp8 == fp8)
       return &e.v;
   return nullptr;
 }

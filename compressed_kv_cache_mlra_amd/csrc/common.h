@@ -150,10 +150,12 @@ struct ProjBatch {
   int32_t page_size, max_pages, num_pages;
   int32_t row_bytes;  // bytes per pool row
   int32_t d_c, d_r;
-  int32_t fp8;        // FP8 E4M3FN latent codes (else bf16)
+  int32_t fp8;        // FP8 E4M3FN latent codes (else bf16): 1 one cache scale, 2 block scales
   float cache_inv;    // FP8: fp32 reciprocal of the cache scale
   void* c_out;        // latent before rounding/encoding: fp32 (FP8) or bf16; may be null
   const uint16_t* kr_src;  // bf16 RoPE keys [B][d_r] to copy into the rows; may be null
+  float* lat;         // fp8 == 2: the fp32 latents [B][d_c], encoded into the rows afterwards
+  int32_t n_blocks;   // fp8 == 2: latent blocks per row
 };
 
 // ------------------------------------------------------------- device helpers

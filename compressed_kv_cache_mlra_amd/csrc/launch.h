@@ -12,14 +12,15 @@ namespace mlra {
 struct MfmaVariant {
   int w, d_r, n_blocks, head_tiles;  // shape key
   int groups, tile_tokens, occupancy;  // tuning (occupancy: workgroups per compute unit)
-  int fp8;                             // the cache holds E4M3FN latent codes
+  int fp8;                             // E4M3FN latent codes: 1 one scale per cache, 2 per token and block
   int threads;
   int lds_bytes;
 };
 
 // Returns the MFMA variant for this shape, or nullptr when only the generic
 // path can run it.
-const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles, bool fp8);
+// fp8: 0 bf16 cache, 1 FP8 with one scale per cache, 2 FP8 with per-token block scales
+const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tiles, int fp8);
 
 hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int32_t* seq_lens,
                          const void* q_c, const void* q_r, const void* w_uk, hipStream_t stream);

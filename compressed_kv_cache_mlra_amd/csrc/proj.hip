@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <initializer_list>
 
 #include "../../include/mlra.h"
@@ -228,6 +229,33 @@ __device__ __forceinline__ uint8_t* pool_row(const ProjBatch& a, int m) {
          (static_cast<int64_t>(phys) * a.page_size + pos % a.page_size) * a.row_bytes;
 }
 
+// Block-scaled FP8 rows of the appended tokens (one workgroup per token, one
+// wave per latent block): the block's scale is its largest magnitude over 448
+// in fp32 (NaN values left out), or 1 where that is 0, below the smallest
+// normal fp32 or not finite; each code is the nearest E4M3FN of c x fp32(1 /
+// scale). Writes the codes, the scales and the row's zero pad; the RoPE key
+// was written by the product's epilogue.
+__global__ __launch_bounds__(256) void encode_block_scaled_kernel(ProjBatch a) {
+  const int m = blockIdx.x;
+  uint8_t* row = pool_row(a, m);
+  if (!row) return;
+  const int w = a.d_c / a.n_blocks;
+  const float* c = a.lat + static_cast<int64_t>(m) * a.d_c;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int j = wave; j < a.n_blocks; j += 4) {
+    float amax = 0.f;
+    for (int i = lane; i < w; i += 64) amax = fmaxf(amax, fabsf(c[j * w + i]));  // fmaxf skips NaN
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float sc = amax / 448.f;
+    if (!(sc >= FLT_MIN) || isinf(sc)) sc = 1.f;
+    const float inv = 1.f / sc;
+    for (int i = lane; i < w; i += 64) row[j * w + i] = static_cast<uint8_t>(e4m3_encode(c[j * w + i] * inv));
+    if (lane == 0) *reinterpret_cast<float*>(row + a.d_c + 2 * a.d_r + 4 * j) = sc;
+  }
+  for (int i = a.d_c + 2 * a.d_r + 4 * a.n_blocks + threadIdx.x; i < a.row_bytes; i += 256) row[i] = 0;
+}
+
 // Output pair (n, n + 1) of sequence m and matrix mat: RoPE (pair index n / 2,
 // angle pos base^(-n / N) in fp64) if the job asks for it, then one rounding,
 // into the job's destination.
@@ -236,9 +264,16 @@ __device__ __forceinline__ void proj_store(const ProjJob& jb, const ProjBatch& a
   if (jb.kind == kProjLatentRow) {
     uint8_t* row = pool_row(a, m);
     if (!row) return;
-    if (a.fp8) {
+    if (a.fp8 == 2) {
+      // block scales need the whole block: keep the fp32 latent for the encoder
+      float* l = a.lat + static_cast<int64_t>(m) * a.d_c + n;
+      l[0] = v0;
+      l[1] = v1;
+    } else if (a.fp8) {
       *reinterpret_cast<uint16_t*>(row + n) =
           static_cast<uint16_t>(e4m3_encode(v0 * a.cache_inv) | (e4m3_encode(v1 * a.cache_inv) << 8));
+    }
+    if (a.fp8) {
       if (a.c_out) {
         float* c = static_cast<float*>(a.c_out) + static_cast<int64_t>(m) * a.d_c + n;
         c[0] = v0;
@@ -640,8 +675,9 @@ void set_pool(mlra::ProjBatch& b, const mlra_desc* d, void* pool, const int32_t*
   b.page_size = d->page_size;
   b.max_pages = d->max_pages_per_seq;
   b.num_pages = d->num_pages;
-  b.fp8 = d->dtype == MLRA_FP8_E4M3;
-  b.row_bytes = b.fp8 ? d->d_c + 2 * d->d_r : 2 * (d->d_c + d->d_r);
+  b.fp8 = mlra::fp8_mode(d);
+  b.row_bytes = b.fp8 ? mlra::fp8_row_bytes(d) : 2 * (d->d_c + d->d_r);
+  b.n_blocks = d->n_blocks;
   b.d_c = d->d_c;
   b.d_r = d->d_r;
   b.cache_inv = 1.0f / (d->cache_scale > 0.f ? d->cache_scale : 1.0f);
@@ -695,9 +731,7 @@ int proj_scratch(const mlra_desc* d, void* workspace, size_t ws_bytes, void** sc
   return MLRA_OK;
 }
 
-}  // namespace
-
-size_t mlra::proj_scratch_bytes(const mlra_desc* d) {
+size_t splitk_scratch_bytes(const mlra_desc* d) {
   if (!elems_bf16(d) || d->d_model < 1 || d->d_model % 8 != 0) return 0;  // VALU path: no scratch
   size_t need = 0;
   if (d->d_c % 8 == 0 && d->d_r % 8 == 0) {
@@ -716,6 +750,29 @@ size_t mlra::proj_scratch_bytes(const mlra_desc* d) {
                               query_batch2(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), kCplQuery2));
   }
   return need;
+}
+
+// Block-scaled FP8 caches: the fp32 latents [B][d_c] between the product and
+// the encoder, after the split-K scratch.
+size_t lat_offset(const mlra_desc* d) { return (splitk_scratch_bytes(d) + 255) / 256 * 256; }
+float* lat_scratch(const mlra_desc* d, void* scratch) {
+  return reinterpret_cast<float*>(static_cast<char*>(scratch) + lat_offset(d));
+}
+
+hipError_t encode_rows(const mlra::ProjBatch& b, hipStream_t stream) {
+  if (b.fp8 != 2) return hipSuccess;
+  mlra::encode_block_scaled_kernel<<<b.B, 256, 0, stream>>>(b);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mlra::proj_scratch_bytes(const mlra_desc* d) {
+  const size_t need = splitk_scratch_bytes(d);
+  // block-scaled appends run on the MFMA product only (d_model % 8 == 0), which
+  // may need no split-K scratch: the latents get their room regardless
+  if (fp8_mode(d) != 2 || d->d_model < 1 || d->d_model % 8 != 0) return need;
+  return lat_offset(d) + sizeof(float) * static_cast<size_t>(d->batch) * d->d_c;
 }
 
 extern "C" int mlra_rope_key(const mlra_desc* desc, const void* x, const void* w_kr,
@@ -833,7 +890,11 @@ int mlra::append_latent_mfma(const mlra_desc* desc, void* pool, const int32_t* p
   const int st = proj_scratch(desc, workspace, ws_bytes, &scratch);
   if (st != MLRA_OK) return st;
   ProjBatch b = append_batch(desc, x, w_dkv, positions, pool, page_table, kr_new, c_out);
-  return proj_status(launch_proj_mfma(b, kCplToken, scratch, static_cast<hipStream_t>(stream)));
+  b.lat = lat_scratch(desc, scratch);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int st2 = proj_status(launch_proj_mfma(b, kCplToken, scratch, s));
+  if (st2 != MLRA_OK) return st2;
+  return proj_status(encode_rows(b, s));
 }
 
 extern "C" int mlra_project_token(const mlra_desc* desc, const void* x, const int32_t* positions, void* pool,
@@ -866,7 +927,9 @@ extern "C" int mlra_project_token(const mlra_desc* desc, const void* x, const in
     return mlra_project_query(desc, x, w_dq, w_uq, w_qr, positions, c_q, q_c, q_r, workspace, ws_bytes, stream);
   }
   ProjBatch b1 = token_batch(desc, x, positions, pool, page_table, w_dkv, w_kr, kr_out, c_out, w_dq, c_q);
+  b1.lat = lat_scratch(desc, scratch);
   st = proj_status(launch_proj_mfma(b1, kCplToken, scratch, s));
+  if (st == MLRA_OK) st = proj_status(encode_rows(b1, s));
   if (st != MLRA_OK || desc->d_cq == 0) return st;
   ProjBatch b2 = query_batch2(desc, c_q, w_uq, w_qr, positions, q_c, q_r);
   return proj_status(launch_proj_mfma(b2, kCplQuery2, scratch, s));

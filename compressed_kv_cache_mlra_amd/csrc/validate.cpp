@@ -8,9 +8,19 @@
 
 namespace mlra {
 
+int fp8_mode(const mlra_desc* d) {
+  return d->dtype == MLRA_FP8_E4M3 ? 1 : d->dtype == MLRA_FP8_E4M3_BS ? 2 : 0;
+}
+
+int fp8_row_bytes(const mlra_desc* d) {
+  const int rb = d->d_c + 2 * d->d_r + (d->dtype == MLRA_FP8_E4M3_BS ? 4 * d->n_blocks : 0);
+  return (rb + 15) / 16 * 16;
+}
+
 int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (!d) return MLRA_ERR_INVALID_ARG;
-  if (d->dtype != MLRA_F32 && d->dtype != MLRA_BF16 && d->dtype != MLRA_FP8_E4M3) return MLRA_ERR_UNSUPPORTED;
+  if (d->dtype != MLRA_F32 && d->dtype != MLRA_BF16 && d->dtype != MLRA_FP8_E4M3 && d->dtype != MLRA_FP8_E4M3_BS)
+    return MLRA_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->n_heads < 1 || d->d_h < 1 || d->d_c < 1 || d->n_blocks < 1 ||
       d->blocks_per_head < 1 || d->d_r < 0 || d->max_pages_per_seq < 1 || d->num_pages < 1)
     return MLRA_ERR_INVALID_ARG;
@@ -26,7 +36,7 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   const int w = d->d_c / d->n_blocks;
   if (d->dtype != MLRA_F32 && (w % 8 != 0 || d->d_r % 8 != 0)) return MLRA_ERR_INVALID_ARG;
   // FP8 rows: d_c code bytes in whole 16-byte chunks, then the bf16 RoPE key
-  if (d->dtype == MLRA_FP8_E4M3 && d->d_c % 16 != 0) return MLRA_ERR_INVALID_ARG;
+  if (fp8_mode(d) && d->d_c % 16 != 0) return MLRA_ERR_INVALID_ARG;
   if (d->dtype == MLRA_FP8_E4M3 && (!(d->cache_scale == d->cache_scale) || isinf(d->cache_scale)))
     return MLRA_ERR_INVALID_ARG;
   if (d->dtype == MLRA_F32 && (w % 4 != 0 || d->d_r % 4 != 0)) return MLRA_ERR_INVALID_ARG;

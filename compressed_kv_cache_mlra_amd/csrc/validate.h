@@ -20,4 +20,10 @@ int check_desc(const mlra_desc* d, ShapeInfo* s);
 // Extra checks of the append entry point.
 int check_append(const mlra_desc* d);
 
+// FP8 caches: 1 per-cache scale, 2 one scale per token and latent block; 0 otherwise.
+int fp8_mode(const mlra_desc* d);
+
+// Bytes of one FP8 cache row (codes, bf16 k^R, block scales, pad to 16).
+int fp8_row_bytes(const mlra_desc* d);
+
 }  // namespace mlra

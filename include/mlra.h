@@ -40,11 +40,17 @@
  *    and the RoPE key in bf16; queries, weights, x and k^R_new are bf16 and
  *    c_out is fp32. It is supported for the shapes with an MFMA attention
  *    variant (MLRA_ERR_UNSUPPORTED otherwise).
+ *    MLRA_FP8_E4M3_BS is the same quantised cache with one fp32 scale per
+ *    token and latent block instead of cache_scale (which it ignores): latent
+ *    value (token, col) = (decoded code) x the scale of col's block in that
+ *    token's row. Same shapes and array types as MLRA_FP8_E4M3.
  *
  * Cache layout (all entry points):
  *  - pool: [num_pages][page_size][d_c + d_r]; row = [c (d_c) | k^R (d_r)].
  *    MLRA_FP8_E4M3: rows of d_c + 2 d_r bytes, [codes (d_c bytes) | k^R (d_r
- *    bf16)].
+ *    bf16)]. MLRA_FP8_E4M3_BS: rows of d_c + 2 d_r + 4 n_blocks bytes rounded
+ *    up to a multiple of 16, [codes | k^R (bf16) | n_blocks fp32 scales |
+ *    zero pad].
  *  - page_table: int32 [batch][max_pages_per_seq]; token t of sequence b lives
  *    in row page_table[b][t / page_size] * page_size + t % page_size.
  *    NULL means the identity layout: page p of sequence b is
@@ -76,7 +82,7 @@ typedef enum {
   MLRA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
 } mlra_status;
 
-typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1, MLRA_FP8_E4M3 = 2 } mlra_dtype;
+typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1, MLRA_FP8_E4M3 = 2, MLRA_FP8_E4M3_BS = 3 } mlra_dtype;
 
 /* Error flags a kernel can raise in the workspace (see mlra_read_flags). */
 #define MLRA_FLAG_BAD_PAGE 1u
@@ -98,7 +104,8 @@ typedef struct {
   float softmax_scale;       /* <= 0 selects 1 / sqrt(d_h + d_r) */
   float out_scale;           /* <= 0 selects 1 / sqrt(blocks_per_head) */
   float cache_scale;         /* MLRA_FP8_E4M3: latent value of a code = decoded code x
-                                cache_scale (<= 0 selects 1); ignored otherwise */
+                                cache_scale (<= 0 selects 1); ignored otherwise (also by
+                                MLRA_FP8_E4M3_BS, whose rows carry their scales) */
   int32_t d_cq;              /* mlra_project_query only: query latent width d_c' */
   float rope_base;           /* RoPE frequency base (<= 0 selects 10000) */
 } mlra_desc;
@@ -124,6 +131,14 @@ size_t mlra_workspace_bytes(const mlra_desc* desc, int32_t max_seq_len);
  *   cache_scale and encoded to the nearest E4M3FN code (ties to even,
  *   magnitudes of 448 and above saturate to 448, NaN to 0x7F); c_out receives
  *   the fp32 latent before encoding.
+ * MLRA_FP8_E4M3_BS: each latent block of the fp32 latent gets the scale
+ *   (largest magnitude of the block) / 448 in fp32, or 1 where that quotient
+ *   is 0, below the smallest normal fp32 or not finite (NaN values are left
+ *   out of the largest magnitude), and is encoded as above with that scale;
+ *   the row's scales and zero pad are written too. Needs the MFMA product
+ *   (bf16 arrays, d_model % 8 == 0, the alignments below), else
+ *   MLRA_ERR_UNSUPPORTED. The workspace also holds the fp32 latents between
+ *   the product and the encoding.
  * A position outside [0, max_pages_per_seq * page_size) writes nothing. The
  * caller advances its sequence lengths itself.
  * workspace: at least mlra_workspace_bytes(desc, .) bytes (the decode's

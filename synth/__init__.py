@@ -128,6 +128,10 @@ WORKLOADS = {
             shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16",
                         d_model=4096, d_cq=1536),
             lengths=("uniform_append", 8191, 8191)),
+    8: dict(name="MLRA-4 fp8-e4m3 cache, one scale per token and block, B=32 h=64 d_h=128 d_c=512(4x128) "
+                 "d_r=64 ctx=8192 paged",
+            shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8b"),
+            lengths=("fixed", 8192)),
 }
 
 

@@ -56,7 +56,7 @@ class GpuProblem:
         if inp.x is not None:
             self.positions = to_dev(inp.positions)
             self.x, self.w_dkv, self.kr_new = to_dev(inp.x), to_dev(inp.w_dkv), to_dev(inp.kr_new)
-            c_dtype = t.float32 if s.dtype == "fp8" else self.pool.dtype  # fp8: latent before encoding
+            c_dtype = t.float32 if s.is_fp8 else self.pool.dtype  # fp8: latent before encoding
             self.c_out = t.empty((s.batch, s.d_c), dtype=c_dtype, device="cuda")
 
     def append(self, stream=None):
@@ -84,17 +84,21 @@ def rms(a):
 
 
 def check_outputs(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out"):
-    """bf16: max |g - r| / RMS(r) <= 2e-2; fp8 caches: <= 3e-2;
+    """bf16: max |g - r| / RMS(r) <= 2e-2; fp8 caches: <= 3e-2 (block-scaled: 5e-2);
     fp32: max |g - r| / max(|r|, RMS(r)) <= 1e-5."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
     r = rms(ref)
-    if dtype in ("bf16", "fp8"):
-        # fp8 caches compute exactly like the bf16 path (bf16 q~ and P, fp32
+    if dtype in ("bf16", "fp8", "fp8b"):
+        # fp8 caches (either scaling) compute exactly like the bf16 path (bf16 q~ and P, fp32
         # accumulation); their bar is what those two roundings produce on the
         # fp8 test inputs: a numpy emulation of just those roundings reaches
         # 2.7e-2 of the RMS on the worst case, so the bar is 3e-2
-        tol = 2e-2 if dtype == "bf16" else 3e-2
+        # block-scaled caches (scales up to 2 per token and block) widen the
+        # logits, so the q~ rounding weighs more: the same emulation, with p s
+        # rounded to bf16, reaches 3.8e-2 and 4.0e-2 of the sequence RMS on the
+        # MLRA-2 test inputs, so their bar is 5e-2
+        tol = {"bf16": 2e-2, "fp8": 3e-2, "fp8b": 5e-2}[dtype]
         err = float(np.max(np.abs(gpu - ref))) / max(r, 1e-30)
         assert err <= tol, f"{what}: max err / rms = {err:.3e}"
     else:
@@ -109,5 +113,5 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, dtype: str):
     assert np.all(gpu[~finite] == ref[~finite])
     if finite.any():
         d = np.abs(gpu[finite] - ref[finite])
-        tol = 5e-2 if dtype in ("bf16", "fp8") else 1e-5 * max(1.0, float(np.max(np.abs(ref[finite]))))
+        tol = 5e-2 if dtype in ("bf16", "fp8", "fp8b") else 1e-5 * max(1.0, float(np.max(np.abs(ref[finite]))))
         assert float(np.max(d)) <= tol, f"lse: max abs err {float(np.max(d)):.3e}"

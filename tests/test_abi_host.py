@@ -231,6 +231,29 @@ def test_fp8_needs_an_mfma_variant_and_aligned_rows():
     assert _decode(nan_scale) == mlra.ERR_INVALID_ARG
 
 
+def test_fp8_block_scaled_descriptor():
+    """Block-scaled FP8 caches: the four MFMA shapes are accepted and other
+    shapes rejected like per-cache FP8; cache_scale is ignored (even NaN); the
+    append's workspace also holds the fp32 latents [B][d_c]; without the MFMA
+    product (d_model not a multiple of 8) the append is unsupported."""
+    L = mlra.lib()
+    for kw in (dict(n_heads=64, d_c=512, n_blocks=4), dict(n_heads=64, d_c=512, n_blocks=1),
+               dict(n_heads=16, d_c=128, n_blocks=1), dict(n_heads=64, d_c=512, n_blocks=2)):
+        ok = _desc(dtype="fp8b", d_h=128, d_r=64, cache_scale=float("nan"), **kw)
+        assert L.mlra_workspace_bytes(ctypes.byref(ok), 10) > 0, kw
+    assert _decode(_desc(dtype="fp8b", n_heads=8, d_h=16, d_c=64, n_blocks=4, d_r=16)) == mlra.ERR_UNSUPPORTED
+    assert _decode(_desc(dtype="fp8b", n_heads=8, d_h=16, d_c=72, n_blocks=1, d_r=16)) == mlra.ERR_INVALID_ARG
+    per_cache = _desc(dtype="fp8", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, d_model=512)
+    blocked = _desc(dtype="fp8b", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, d_model=512)
+    extra = L.mlra_workspace_bytes(ctypes.byref(blocked), 10) - L.mlra_workspace_bytes(ctypes.byref(per_cache), 10)
+    assert 4 * blocked.batch * 512 <= extra <= 4 * blocked.batch * 512 + 256
+    assert mlra.fp8_row_bytes(blocked) == 656 and mlra.fp8_row_bytes(per_cache) == 640
+    valu = _desc(dtype="fp8b", n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, d_model=500)
+    ws = ctypes.c_size_t(L.mlra_workspace_bytes(ctypes.byref(valu), 10))
+    st = L.mlra_append_latent(ctypes.byref(valu), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert st == mlra.ERR_UNSUPPORTED
+
+
 def test_rope_key_validation():
     L = mlra.lib()
     d = _desc(d_model=64)

@@ -20,6 +20,7 @@ MLRA4 = dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64)
 STEP_SHAPES = {
     "mlra4-bf16": dict(MLRA4, dtype="bf16"),
     "mlra4-fp8": dict(MLRA4, dtype="fp8", cache_scale=0.5),
+    "mlra4-fp8b": dict(MLRA4, dtype="fp8b"),                         # per-token block scales
     "mla-bf16": dict(MLRA4, n_blocks=1, dtype="bf16"),
     "mlra4-k2-bf16": dict(MLRA4, dtype="bf16", blocks_per_head=2),  # two blocks per head
     "mlra4-f32": dict(MLRA4, dtype="f32"),                          # generic kernels

@@ -31,7 +31,9 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run_and_compare(inp, pairs=None, lse=True):
+def _run_and_compare(inp, pairs=None, lse=True, per_sequence=False):
+    """per_sequence: each sequence's outputs against that sequence's own RMS
+    (ragged batches, where a short sequence's outputs are many times larger)."""
     prob = _gpu.GpuProblem(inp)
     out, l = prob.run()
     s = inp.shape
@@ -40,7 +42,16 @@ def _run_and_compare(inp, pairs=None, lse=True):
     ref, rl = oracle.decode_unabsorbed(inp, pairs)
     g = np.stack([out[b, i] for b, i in pairs])
     gl = np.stack([l[b, i] for b, i in pairs])
-    err = _gpu.check_outputs(g, ref, s.dtype)
+    if per_sequence:
+        err = 0.0
+        for b in sorted({b for b, _ in pairs}):
+            rows = [k for k, (bb, _) in enumerate(pairs) if bb == b]
+            if int(inp.seq_lens[b]) == 0:
+                assert np.all(g[rows] == 0)
+                continue
+            err = max(err, _gpu.check_outputs(g[rows], ref[rows], s.dtype, f"sequence {b}"))
+    else:
+        err = _gpu.check_outputs(g, ref, s.dtype)
     if lse:
         _gpu.check_lse(gl, rl, s.dtype)
     return prob, err
@@ -342,6 +353,71 @@ def test_fp8_append_encodes_kernel_latent():
     assert np.array_equal(before[~changed], after[~changed])
 
 
+# ------------------------------------ FP8 cache, one scale per token and block
+
+@pytest.mark.parametrize("name", list(FP8_SHAPES))
+def test_fp8b_small_all_outputs(name):
+    """Block-scaled FP8 caches (scales 2^u, u in [-3, 1), per token and block;
+    NaN codes, keys and scales in unused rows) against the oracle on every
+    output and lse, for each of the four kernel shapes. Sequence by sequence:
+    p_t s_t is rounded to bf16 even for a one-token sequence (a power-of-two
+    cache scale made that exact), and such a sequence's outputs are many times
+    the batch RMS."""
+    kw, lens = FP8_SHAPES[name]
+    kw = dict(kw, dtype="fp8b")
+    kw.pop("cache_scale")
+    _say(f"case: fp8b {name}, lengths {lens}")
+    s = synth.Shape(batch=len(lens), **kw)
+    inp = synth.make_inputs(s, ("list", lens), 4300 + len(name))
+    _, err = _run_and_compare(inp, per_sequence=True)
+    _say(f"fp8b {name}: max err/rms {err:.2e}")
+
+
+def test_fp8b_full_size_sampled():
+    _say("case: full-size fp8b workload (MLRA-4 shape, B=32, 8K)")
+    inp = synth.workload_inputs(8)
+    rng = np.random.default_rng(8)
+    s = inp.shape
+    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
+    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
+    _, err = _run_and_compare(inp, pairs)
+    _say(f"fp8b full: max err/rms {err:.2e}")
+
+
+def test_fp8b_append_encodes_each_block():
+    """Block-scaled append: c_out within the fp32 bar of the oracle's latent;
+    every block's codes and scale bit-identical to the oracle's block encoding
+    of the kernel's own fp32 latent; RoPE key, zero pad, no other byte changed.
+    One token's latent is all zero in one block (scale 1, zero codes)."""
+    _say("case: fp8b append")
+    s = synth.Shape(batch=5, n_heads=8, d_h=32, d_c=512, n_blocks=4, d_r=64, dtype="fp8b", d_model=1000)
+    inp = synth.make_inputs(s, ("list_append", [0, 63, 64, 127, 500]), 79)
+    inp.w_dkv[:, 128:256] = 0  # block 1 of every token is exactly zero
+    prob = _gpu.GpuProblem(inp)
+    before = prob.pool.cpu().numpy().copy()
+    prob.append()
+    after = prob.pool.cpu().numpy()
+    c_gpu = prob.c_out.cpu().numpy()
+    c_ref = oracle.append(inp, inp.pool.copy())
+    err = np.abs(c_gpu.astype(np.float64) - c_ref) / np.maximum(np.abs(c_ref), _gpu.rms(c_ref))
+    assert err.max() <= 1e-5, err.max()
+    o = s.d_c + 2 * s.d_r
+    changed = np.zeros(before.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // 64], pos % 64
+        changed[pg, off] = True
+        row = after[pg, off]
+        for j in range(s.n_blocks):
+            codes, sc = oracle.fp8_block_encode(c_gpu[b, j * s.w:(j + 1) * s.w])
+            assert np.array_equal(row[j * s.w:(j + 1) * s.w], codes), (b, j)
+            assert row[o + 4 * j:o + 4 * j + 4].view(np.float32)[0] == sc, (b, j)
+        assert row[o + 4:o + 8].view(np.float32)[0] == 1.0 and np.all(row[s.w:2 * s.w] & 0x7F == 0)
+        assert np.all(row[o + 4 * s.n_blocks:] == 0)
+        assert np.array_equal(row[s.d_c:o].view(np.uint16), inp.kr_new[b])
+    assert np.array_equal(before[~changed], after[~changed])
+
+
 # The tuned kernel of each configured shape (step order, two-tile prologue and
 # column splits differ between them), on inputs that stress the unit plan:
 # many short and empty sequences, so work units span several sequences (the
@@ -353,6 +429,7 @@ VARIANT_SHAPES = {
     "tp-share": dict(n_heads=16, d_h=128, d_c=128, n_blocks=1, d_r=64, dtype="bf16"),
     "mlra2": dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="bf16"),
     "mlra4-fp8": dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8", cache_scale=0.5),
+    "mlra4-fp8b": dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8b"),
 }
 
 

@@ -60,6 +60,9 @@ QP_SHAPES = {
                 d_model=300, d_cq=40),
     "fp8-cache": dict(batch=5, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8",
                       cache_scale=0.125, d_model=512, d_cq=256, rope_base=500.0),
+    # one scale per token and latent block
+    "fp8b-cache": dict(batch=5, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8b",
+                       d_model=512, d_cq=256, rope_base=500.0),
 }
 
 
@@ -193,7 +196,7 @@ def test_full_size_layer_workload():
     _say(f"  full-size layer step: out max err/rms {err:.2e}")
 
 
-@pytest.mark.parametrize("name", ["bf16-mlra4", "bf16-wide", "fp8-cache"])
+@pytest.mark.parametrize("name", ["bf16-mlra4", "bf16-wide", "fp8-cache", "fp8b-cache"])
 def test_project_token_fused(name):
     """mlra_project_token: the latent append, the RoPE key and the query path
     of the new token in one call. k^R, q^C and q^R against the oracle; the
@@ -206,7 +209,7 @@ def test_project_token_fused(name):
     prob = _gpu.GpuProblem(inp)
     desc = prob.desc
     et = mlra._elem_dtype(desc)
-    fp8 = s.dtype == "fp8"
+    fp8 = s.is_fp8
     cq = t.empty((s.batch, s.d_cq), dtype=t.float32, device="cuda")
     qc = t.empty((s.batch, s.n_heads, s.d_h), dtype=et, device="cuda")
     qr = t.empty((s.batch, s.n_heads, s.d_r), dtype=et, device="cuda")
@@ -237,9 +240,19 @@ def test_project_token_fused(name):
         if fp8:
             err = np.abs(c_gpu[b].astype(np.float64) - c_ref[b]) / max(_gpu.rms(c_ref), 1e-30)
             assert err.max() <= 1e-5, err.max()
-            codes = oracle.e4m3_encode_array(c_gpu[b] * np.float32(1.0 / s.cache_scale))
-            assert np.array_equal(row[:s.d_c], codes)
-            assert np.array_equal(row[s.d_c:].view(np.uint16), kr_b[b])
+            if s.dtype == "fp8b":
+                # each block: the oracle's block encoding of the kernel's own fp32 latent
+                o = s.d_c + 2 * s.d_r
+                for j in range(s.n_blocks):
+                    codes, sc = oracle.fp8_block_encode(c_gpu[b, j * s.w:(j + 1) * s.w])
+                    assert np.array_equal(row[j * s.w:(j + 1) * s.w], codes)
+                    assert row[o + 4 * j:o + 4 * j + 4].view(np.float32)[0] == sc
+                assert np.all(row[o + 4 * s.n_blocks:] == 0)
+                assert np.array_equal(row[s.d_c:o].view(np.uint16), kr_b[b])
+            else:
+                codes = oracle.e4m3_encode_array(c_gpu[b] * np.float32(1.0 / s.cache_scale))
+                assert np.array_equal(row[:s.d_c], codes)
+                assert np.array_equal(row[s.d_c:].view(np.uint16), kr_b[b])
         else:
             assert np.abs(c_gpu[b].astype(np.int32) - c_ref[b].astype(np.int32)).max() <= 1
             assert np.array_equal(row[:s.d_c], c_gpu[b])
