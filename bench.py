@@ -54,7 +54,7 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    p.add_argument("--workload", type=int, default=2, choices=list(range(1, 13)))
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -132,6 +132,22 @@ WORKLOADS = {
                  "d_r=64 ctx=8192 paged",
             shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8b"),
             lengths=("fixed", 8192)),
+    9: dict(name="MLRA-4 reading B (k=2: each head attends 2 blocks), bf16, B=32 h=64 d_h=128 d_c=512(4x128) "
+                 "d_r=64 ctx=8192 paged",
+            shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16", blocks_per_head=2),
+            lengths=("fixed", 8192)),
+    10: dict(name="MLRA-4 reading B (k=4: each head attends all 4 blocks), bf16, B=32 h=64 d_h=128 "
+                  "d_c=512(4x128) d_r=64 ctx=8192 paged",
+             shape=Shape(batch=32, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16", blocks_per_head=4),
+             lengths=("fixed", 8192)),
+    11: dict(name="MLRA-4 at the paper's model width h=24 (6 heads per block), bf16, B=32 d_h=128 "
+                  "d_c=512(4x128) d_r=64 ctx=8192 paged",
+             shape=Shape(batch=32, n_heads=24, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16"),
+             lengths=("fixed", 8192)),
+    12: dict(name="MLRA-4 reading B (k=4) at h=24 (24 heads per block), bf16, B=32 d_h=128 d_c=512(4x128) "
+                  "d_r=64 ctx=8192 paged",
+             shape=Shape(batch=32, n_heads=24, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16", blocks_per_head=4),
+             lengths=("fixed", 8192)),
 }
 
 
