@@ -287,6 +287,21 @@ def test_graph_replay_matches_eager():
 
 
 
+@pytest.mark.parametrize("wl", [9, 10, 11, 12])
+def test_reading_b_and_h24_full_size_sampled(wl):
+    """Reading B (k = 2, 4) and the 24-head width at full size (B = 32, 8192
+    tokens, the launches bench.py times): sampled (sequence, head) pairs,
+    including the last head, against the oracle; outputs and every block's lse."""
+    _say(f"case: full-size workload {wl}")
+    inp = synth.workload_inputs(wl)
+    s = inp.shape
+    rng = np.random.default_rng(wl)
+    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
+    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
+    _, err = _run_and_compare(inp, pairs)
+    _say(f"workload {wl} full: max err/rms {err:.2e}")
+
+
 # ------------------------------------------------------------------ FP8 cache
 
 FP8_SHAPES = {
