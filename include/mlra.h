@@ -246,8 +246,9 @@ int mlra_project_query(const mlra_desc* desc, const void* x, const void* w_dq, c
  * one call: the same results as mlra_rope_key (into kr_out), then
  * mlra_append_latent with kr_new = kr_out, then (d_cq > 0) mlra_project_query.
  * On the MFMA path the three products over x (W^DKV, W^KR, W^DQ) share one
- * launch and the pool row, k^R and c^Q are written by its epilogue; the query
- * up-projections take a second launch. w_dq, w_uq, w_qr, c_q, q_c and q_r may
+ * launch and the pool row, k^R and c^Q are written by its epilogue (a
+ * block-scaled FP8 cache's codes and scales by a small encoding launch right
+ * after it); the query up-projections take a second launch. w_dq, w_uq, w_qr, c_q, q_c and q_r may
  * be NULL when d_cq == 0; c_out may be NULL. Same layouts, element types and
  * workspace as the three calls. */
 int mlra_project_token(const mlra_desc* desc, const void* x, const int32_t* positions, void* pool,
