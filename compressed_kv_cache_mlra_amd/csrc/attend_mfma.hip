@@ -47,7 +47,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false, bool CF_ = false,
-          int CS_ = 1, bool P2_ = false, bool TS_ = false>
+          int CS_ = 1, bool P2_ = false, bool TS_ = false, int HPW_ = 1>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -82,7 +82,11 @@ struct Cfg {
   static constexpr int ROWB = (ROWG + 127) / 128 * 128;
   static constexpr int CPRG = ROWG / 16;                     // 16-byte HBM chunks per row
   static constexpr int LATC = F8 ? NBR * W / 16 : 0;         // HBM chunks of latent codes per row
-  static constexpr int TASKS = NBR * HT;
+  // Head tiles per wave: HPW > 1 gives each wave HPW of its block's 16-head
+  // tiles, so every LDS operand read serves HPW MFMAs and the workgroup needs
+  // HPW times fewer waves (more registers each).
+  static constexpr int HPW = HPW_;
+  static constexpr int TASKS = NBR * HT / HPW;
   static constexpr int NWAVES = TASKS * G * CS;
   static constexpr int NTHREADS = NWAVES * 64;
   // waves per SIMD when OCC workgroups share a compute unit (the second
@@ -119,6 +123,7 @@ struct Cfg {
   static_assert(!TS || (F8 && NBR <= 4 && CS == 1 && SCO % 16 == 0), "token scales: one chunk, no splits");
   static_assert(PT_CAP >= 64, "LDS: room for the page-id table");
   static_assert(NTHREADS <= 1024, "");
+  static_assert(HT % HPW == 0 && (HPW == 1 || CS == 1), "head tiles per wave: whole tiles, no column splits");
 };
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
@@ -212,17 +217,22 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   const int tgrp = C::CS > 1 ? (wave / C::TASKS) % C::G : wave / C::TASKS;
   // column split: value columns [cs W / CS, (cs + 1) W / CS) (a constant 0 without splits)
   const int cs = C::CS > 1 ? wave / (C::TASKS * C::G) : 0;
-  const int blk = task / C::HT;
-  const int ht = task % C::HT;
+  constexpr int HW = C::HPW;
+  const int blk = task / (C::HT / HW);
+  const int ht0 = (task % (C::HT / HW)) * HW;  // this wave's first head tile
   const int hgrp = blk / a.k;
   const int jj = blk - hgrp * a.k;
   const int m16 = lane & 15;
   const int g4 = lane >> 4;
-  const int hloc = ht * 16 + m16;
-  const bool head_ok = hloc < a.hpb;
-  const int head = hgrp * a.hpb + hloc;
   const int HK = a.n_heads * a.k;
-  const int hk = head * a.k + jj;
+  bool head_ok[HW];
+  int hk[HW];
+#pragma unroll
+  for (int hw = 0; hw < HW; ++hw) {
+    const int hloc = (ht0 + hw) * 16 + m16;
+    head_ok[hw] = hloc < a.hpb;
+    hk[hw] = (hgrp * a.hpb + hloc) * a.k + jj;
+  }
   const int P = a.page_size;
   const bool loader = tid < C::NLT;
 
@@ -324,13 +334,18 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   };
 
   // ---- compute state
-  floatx4_t O[C::NQ][8];
+  floatx4_t O[HW][C::NQ][8];
+  float m_run[HW], l_run[HW];
 #pragma unroll
-  for (int q = 0; q < C::NQ; ++q)
+  for (int hw = 0; hw < HW; ++hw) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) O[q][e] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  bf16x8_t Qb[C::KKH];  // this wave's score k-steps [cs KKH, (cs + 1) KKH)
+    for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[hw][q][e] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[hw] = -INFINITY;
+    l_run[hw] = 0.f;
+  }
+  bf16x8_t Qb[HW][C::KKH];  // this wave's score k-steps [cs KKH, (cs + 1) KKH), per head tile
 
   int cb = lo;
   int32_t cb_start = pb_start, cb_end = pb_end, cb_n = pb_n;
@@ -341,14 +356,17 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   const uint16_t* qext = reinterpret_cast<const uint16_t*>(a.ws + a.off_qext);
 
   auto load_q = [&](int b) __attribute__((always_inline)) {
-    const uint16_t* qe = qext + (static_cast<int64_t>(b) * HK + hk) * (C::W + C::DR);
 #pragma unroll
-    for (int u = 0; u < C::KKH; ++u) {
-      const int kk = cs * C::KKH + u;
-      const int off = kk < C::KKC ? 32 * kk + 8 * g4 : C::W + 32 * (kk - C::KKC) + 8 * g4;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (head_ok) v = gload16(reinterpret_cast<const uint8_t*>(qe + off));
-      Qb[u] = __builtin_bit_cast(bf16x8_t, v);
+    for (int hw = 0; hw < HW; ++hw) {
+      const uint16_t* qe = qext + (static_cast<int64_t>(b) * HK + hk[hw]) * (C::W + C::DR);
+#pragma unroll
+      for (int u = 0; u < C::KKH; ++u) {
+        const int kk = cs * C::KKH + u;
+        const int off = kk < C::KKC ? 32 * kk + 8 * g4 : C::W + 32 * (kk - C::KKC) + 8 * g4;
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (head_ok[hw]) v = gload16(reinterpret_cast<const uint8_t*>(qe + off));
+        Qb[hw][u] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
   };
   load_q(cb);
@@ -479,7 +497,9 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       const uint8_t* rp0 = sb + r0 * C::ROWB;
       const uint8_t* rp1 = rp0 + 16 * C::ROWB;
       const int key = m16 & 7;
-      floatx4_t S0 = floatx4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+      floatx4_t S0[HW], S1[HW];
+#pragma unroll
+      for (int hw = 0; hw < HW; ++hw) S0[hw] = S1[hw] = floatx4_t{0.f, 0.f, 0.f, 0.f};
       // TS: the scales of this wave's block for its eight tokens (rows past
       // the sequence end were stored as zeros)
       float sc0[4], sc1[4];
@@ -519,16 +539,19 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         for (int u = 0; u < KB; ++u) {
           const int kl = kb + u;
           if (kl < C::KKH) {
-            S0 = mfma32(__builtin_bit_cast(bf16x8_t, A0[u]), Qb[kl], S0);
-            S1 = mfma32(__builtin_bit_cast(bf16x8_t, A1[u]), Qb[kl], S1);
-            if constexpr (C::TS) {
-              if (kl == C::KKC - 1) {
-                // the latent part is complete: scale it per token before the
-                // RoPE k-steps add theirs
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  S0[i] *= sc0[i];
-                  S1[i] *= sc1[i];
+            for (int hw = 0; hw < HW; ++hw) {
+              S0[hw] = mfma32(__builtin_bit_cast(bf16x8_t, A0[u]), Qb[hw][kl], S0[hw]);
+              S1[hw] = mfma32(__builtin_bit_cast(bf16x8_t, A1[u]), Qb[hw][kl], S1[hw]);
+              if constexpr (C::TS) {
+                if (kl == C::KKC - 1) {
+                  // the latent part is complete: scale it per token before the
+                  // RoPE k-steps add theirs
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    S0[hw][i] *= sc0[i];
+                    S1[hw][i] *= sc1[i];
+                  }
                 }
               }
             }
@@ -540,8 +563,8 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         // every split, so all of them see identical scores)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          xch[wave][i][lane] = S0[i];
-          xch[wave][4 + i][lane] = S1[i];
+          xch[wave][i][lane] = S0[0][i];
+          xch[wave][4 + i][lane] = S1[0][i];
         }
         __syncthreads();
 #pragma unroll
@@ -550,8 +573,8 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           const int w2 = task + C::TASKS * (tgrp + C::G * c2);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            S0[i] += xch[w2][i][lane];
-            S1[i] += xch[w2][4 + i][lane];
+            S0[0][i] += xch[w2][i][lane];
+            S1[0][i] += xch[w2][4 + i][lane];
           }
         }
       }
@@ -573,48 +596,52 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // the first 128-column group, read while the scores finish
       u32x4_t R[8];
       read_rows(cs * C::NQ, R);
-      if (valid < C::TT) {
+      bf16x8_t pb[HW];
+#pragma unroll
+      for (int hw = 0; hw < HW; ++hw) {
+        if (valid < C::TT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (rowbase + 4 * g4 + i >= valid) S0[hw][i] = -INFINITY;
+            if (rowbase + 16 + 4 * g4 + i >= valid) S1[hw][i] = -INFINITY;
+          }
+        }
+        // ---- online softmax (per head m16; lanes m16, m16+16, +32, +48 share a head)
+        float mx = fmaxf(fmaxf(fmaxf(S0[hw][0], S0[hw][1]), fmaxf(S0[hw][2], S0[hw][3])),
+                         fmaxf(fmaxf(S1[hw][0], S1[hw][1]), fmaxf(S1[hw][2], S1[hw][3])));
+        mx = max_4lanes(mx);
+        const float m_new = fmaxf(m_run[hw], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float scale = fast_exp2(m_run[hw] - m_use);
+        float p0[4], p1[4];
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (rowbase + 4 * g4 + i >= valid) S0[i] = -INFINITY;
-          if (rowbase + 16 + 4 * g4 + i >= valid) S1[i] = -INFINITY;
+          p0[i] = fast_exp2(S0[hw][i] - m_use);
+          p1[i] = fast_exp2(S1[hw][i] - m_use);
+          psum += p0[i] + p1[i];
         }
-      }
-      // ---- online softmax (per head m16; lanes m16, m16+16, +32, +48 share a head)
-      float mx = fmaxf(fmaxf(fmaxf(S0[0], S0[1]), fmaxf(S0[2], S0[3])),
-                       fmaxf(fmaxf(S1[0], S1[1]), fmaxf(S1[2], S1[3])));
-      mx = max_4lanes(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float scale = fast_exp2(m_run - m_use);
-      float p0[4], p1[4];
-      float psum = 0.f;
+        l_run[hw] = l_run[hw] * scale + psum;
+        m_run[hw] = m_new;
+        if (__any(scale != 1.f)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p0[i] = fast_exp2(S0[i] - m_use);
-        p1[i] = fast_exp2(S1[i] - m_use);
-        psum += p0[i] + p1[i];
-      }
-      l_run = l_run * scale + psum;
-      m_run = m_new;
-      if (__any(scale != 1.f)) {
+          for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
-        for (int q = 0; q < C::NQ; ++q)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) O[q][e] *= scale;
-      }
-      if constexpr (C::TS) {
-        // value side: sum_t p_t (s_t code_t) = sum_t (p_t s_t) code_t; the
-        // softmax sum above keeps the unscaled p_t
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p0[i] *= sc0[i];
-          p1[i] *= sc1[i];
+            for (int e = 0; e < 8; ++e) O[hw][q][e] *= scale;
         }
+        if constexpr (C::TS) {
+          // value side: sum_t p_t (s_t code_t) = sum_t (p_t s_t) code_t; the
+          // softmax sum above keeps the unscaled p_t
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p0[i] *= sc0[i];
+            p1[i] *= sc1[i];
+          }
+        }
+        const u32x4_t pbu = u32x4_t{pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                                    pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
+        pb[hw] = __builtin_bit_cast(bf16x8_t, pbu);
       }
-      const u32x4_t pbu = u32x4_t{pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
-                                  pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbu);
       // ---- values: O^T[col][head] += C^T[col][tokens] P^T[tokens][head]
 #pragma unroll
       for (int q = 0; q < C::NQ; ++q) {
@@ -626,60 +653,67 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             Av[u] = __builtin_amdgcn_perm(R[2 * u + 1][e >> 1], R[2 * u][e >> 1], sel);
-          O[q][e] = mfma32(__builtin_bit_cast(bf16x8_t, Av), pb, O[q][e]);
+#pragma unroll
+          for (int hw = 0; hw < HW; ++hw)
+            O[hw][q][e] = mfma32(__builtin_bit_cast(bf16x8_t, Av), pb[hw], O[hw][q][e]);
         }
       }
     }
 
     if (x + 1 == cb_end || x + 1 == x1) {
-      // ---- segment end: write this wave's partial and reset.
-      const float l_tot = sum_4lanes(l_run);
+      // ---- segment end: write this wave's partials and reset.
       const int64_t slot = static_cast<int64_t>(unit + cb) * C::G + tgrp;
-      // The head's row of weighted sums is scaled by 2^-s, s the exponent of
-      // its largest magnitude, and stored as fp16 (values in (-1, 1), 11-bit
-      // precision); m + s and l 2^-s go with it, which leaves every ratio the
-      // combine forms unchanged.
-      float amax = 0.f;
 #pragma unroll
-      for (int q = 0; q < C::NQ; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(O[q][e][i]));
-      amax = max_4lanes(amax);
-      if constexpr (C::CS > 1) {
-        // the column splits of a head agree on one scale
-        if (g4 == 0) amax_sh[wave][m16] = amax;
-        __syncthreads();
-#pragma unroll
-        for (int c2 = 0; c2 < C::CS; ++c2) amax = fmaxf(amax, amax_sh[task + C::TASKS * (tgrp + C::G * c2)][m16]);
-      }
-      int sexp = 0;
-      if (amax > 0.f) frexpf(amax, &sexp);
-      const float rs = ldexpf(1.f, -sexp);
-      if (head_ok) {
-        // column 128 q + 8 (4 g4 + i) + e holds O[q][e][i]: 8 consecutive
-        // columns per (q, i), one 16-byte store
-        uint16_t* dst = po + (slot * HK + hk) * C::W;
+      for (int hw = 0; hw < HW; ++hw) {
+        const float l_tot = sum_4lanes(l_run[hw]);
+        // The head's row of weighted sums is scaled by 2^-s, s the exponent of
+        // its largest magnitude, and stored as fp16 (values in (-1, 1), 11-bit
+        // precision); m + s and l 2^-s go with it, which leaves every ratio the
+        // combine forms unchanged.
+        float amax = 0.f;
 #pragma unroll
         for (int q = 0; q < C::NQ; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4_t v = {pack_f16x2(O[q][0][i] * rs, O[q][1][i] * rs), pack_f16x2(O[q][2][i] * rs, O[q][3][i] * rs),
-                               pack_f16x2(O[q][4][i] * rs, O[q][5][i] * rs), pack_f16x2(O[q][6][i] * rs, O[q][7][i] * rs)};
-            *reinterpret_cast<u32x4_t*>(dst + 128 * (cs * C::NQ + q) + 8 * (4 * g4 + i)) = v;
-          }
-        if (g4 == 0 && cs == 0) {
-          pm[slot * HK + hk] = m_run + static_cast<float>(sexp);
-          pl[slot * HK + hk] = l_tot * rs;
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(O[hw][q][e][i]));
+        amax = max_4lanes(amax);
+        if constexpr (C::CS > 1) {
+          // the column splits of a head agree on one scale
+          if (g4 == 0) amax_sh[wave][m16] = amax;
+          __syncthreads();
+#pragma unroll
+          for (int c2 = 0; c2 < C::CS; ++c2) amax = fmaxf(amax, amax_sh[task + C::TASKS * (tgrp + C::G * c2)][m16]);
         }
+        int sexp = 0;
+        if (amax > 0.f) frexpf(amax, &sexp);
+        const float rs = ldexpf(1.f, -sexp);
+        if (head_ok[hw]) {
+          // column 128 q + 8 (4 g4 + i) + e holds O[q][e][i]: 8 consecutive
+          // columns per (q, i), one 16-byte store
+          uint16_t* dst = po + (slot * HK + hk[hw]) * C::W;
+#pragma unroll
+          for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const u32x4_t v = {pack_f16x2(O[hw][q][0][i] * rs, O[hw][q][1][i] * rs),
+                                 pack_f16x2(O[hw][q][2][i] * rs, O[hw][q][3][i] * rs),
+                                 pack_f16x2(O[hw][q][4][i] * rs, O[hw][q][5][i] * rs),
+                                 pack_f16x2(O[hw][q][6][i] * rs, O[hw][q][7][i] * rs)};
+              *reinterpret_cast<u32x4_t*>(dst + 128 * (cs * C::NQ + q) + 8 * (4 * g4 + i)) = v;
+            }
+          if (g4 == 0 && cs == 0) {
+            pm[slot * HK + hk[hw]] = m_run[hw] + static_cast<float>(sexp);
+            pl[slot * HK + hk[hw]] = l_tot * rs;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) O[hw][q][e] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[hw] = -INFINITY;
+        l_run[hw] = 0.f;
       }
-#pragma unroll
-      for (int q = 0; q < C::NQ; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[q][e] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      m_run = -INFINITY;
-      l_run = 0.f;
     }
     if constexpr (C::CF) {
       // tile x+1 has been in flight since the previous step; its buffer was
@@ -707,9 +741,9 @@ struct Entry {
 };
 
 template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1,
-          bool P2 = false, bool TS = false>
+          bool P2 = false, bool TS = false, int HPW = 1>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2, TS>;
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2, TS, HPW>;
   return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? (TS ? 2 : 1) : 0, C::NTHREADS, 2 * C::TILE_BYTES},
                &run_variant<C>};
 }
@@ -735,7 +769,10 @@ const Entry kVariants[] = {
     // step of the four combinations of split and prologue measured
     entry<256, 64, 2, 2, 1, 32, 1, false, true, 2, true>(),
     entry<128, 64, 4, 2, 1, 32, 1>(),   // 4 x 128 latent, <= 32 heads per block
-    entry<128, 64, 4, 4, 1, 32, 1>(),   // 4 x 128 latent, <= 64 heads per block
+    // 4 x 128 latent, <= 64 heads per block (reading B with k = 4): two head
+    // tiles per wave, eight waves (sixteen one-tile waves had 128 VGPRs each
+    // and spilled; measured 142 -> 82 us at B = 32, 8K)
+    entry<128, 64, 4, 4, 1, 32, 1, false, false, 1, false, false, 2>(),
     entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
     // FP8 (E4M3FN) caches of the same shapes and tunings
     entry<128, 64, 4, 1, 1, 32, 2, true, true, 1, true>(),
