@@ -511,7 +511,9 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           sc1[i] = *reinterpret_cast<const float*>(sb + t1 * C::ROWB + 16 * ((C::SCO / 16) ^ (t1 & 7)) + 4 * blk);
         }
       }
-      constexpr int KB = 3;  // score k-steps whose operands are read ahead together
+      // score k-steps whose operands are read ahead together (two with two head
+      // tiles per wave: fewer live operands where registers spill; 1-2% faster)
+      constexpr int KB = C::HPW > 1 ? 2 : 3;
 #pragma unroll
       for (int kb = 0; kb < C::KKH; kb += KB) {
         u32x4_t A0[KB], A1[KB];
