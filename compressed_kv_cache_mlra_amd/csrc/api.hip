@@ -54,7 +54,10 @@ int make_plan(const mlra_desc* d, Plan* p) {
   }
   p->units = compute_units() * (p->variant ? p->variant->occupancy : 1);
   p->slots = static_cast<int64_t>(p->units + d->batch) * p->groups + 1;  // + the empty slot
-  const size_t qelem = p->q_bf16 ? 2 : 4;
+  // absorbed-query row: 4 w + 2 d_r bytes on the MFMA path (bf16 hi + lo, or
+  // fp16 + a row scale, and the bf16 RoPE part), fp32 [w + d_r] otherwise
+  const size_t qrow = p->q_bf16 ? 4 * static_cast<size_t>(s.w) + 2 * static_cast<size_t>(d->d_r)
+                                : 4 * static_cast<size_t>(s.w + d->d_r);
   size_t off = align_up(sizeof(WsHeader));
   p->off_cum = off;
   off = align_up(off + sizeof(int32_t) * (d->batch + 1));
@@ -65,7 +68,7 @@ int make_plan(const mlra_desc* d, Plan* p) {
   p->off_udesc = off;
   off = align_up(off + sizeof(int32_t) * kUnitDescInts * static_cast<size_t>(p->units));
   p->off_qext = off;
-  off = align_up(off + qelem * static_cast<size_t>(d->batch) * s.hk * (s.w + d->d_r));
+  off = align_up(off + qrow * static_cast<size_t>(d->batch) * s.hk);
   p->off_pm = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(p->slots) * s.hk);
   p->off_pl = off;
@@ -114,6 +117,7 @@ DecodeArgs decode_args(const mlra_desc* d, const Plan& p, const void* pool, cons
   a.off_pl = static_cast<int64_t>(p.off_pl);
   a.off_po = static_cast<int64_t>(p.off_po);
   a.po_f16 = p.variant ? 1 : 0;
+  a.q_mode = !p.variant ? kQueryF32 : (fp8_mode(d) ? kQueryF16 : kQuerySplit);
   a.batch = d->batch;
   a.n_heads = d->n_heads;
   a.d_h = d->d_h;

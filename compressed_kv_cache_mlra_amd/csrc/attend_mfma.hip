@@ -22,6 +22,11 @@
 //    four tokens of one head in each lane, which is exactly the B-operand
 //    layout of the value product, so P never leaves registers. Per-head max
 //    and sum reduce across the four lanes of a head with v_permlane16/32_swap.
+//  - Precision: the latent part of the absorbed query enters the score MFMAs
+//    as two bf16 parts (hi + lo, about 16 significant bits); the RoPE part is
+//    the bf16 query as given; the fp32 sums are then scaled by softmax_scale
+//    log2(e). (One bf16 rounding of the absorbed query moves the outputs by up
+//    to ~2% of their RMS on short contexts; P stays bf16, ~0.8%.)
 //  - Values: O^T[col][head] += C^T[col][token] P^T[token][head], again
 //    16x16x32 bf16 MFMA; C^T operands come from 128-bit LDS reads of 8 token
 //    rows, transposed in registers with v_perm_b32.
@@ -31,8 +36,12 @@
 //    issues no scalar loads.
 //  - FP8 caches: rows enter LDS as stored (E4M3FN latent codes, then the bf16
 //    k^R), 44% fewer LDS bytes per tile than widened rows; each latent operand
-//    is an 8-byte LDS read widened to 8 bf16 values in registers (exact: every
-//    E4M3 value is a bf16 value).
+//    is an 8-byte LDS read widened to 8 fp16 values in registers (exact: every
+//    E4M3 value is an fp16 value), so the latent products run on
+//    v_mfma_f32_16x16x32_f16 with the absorbed query in fp16 (scaled per row
+//    by a power of two into [1, 2), 11 significant bits) and P in fp16; with
+//    block scales the value side takes P s 2^-E (E a running exponent of the
+//    largest scale, folded back into the partial's max).
 #include <type_traits>
 
 #include "common.h"
@@ -43,6 +52,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -108,6 +118,13 @@ struct Cfg {
   static constexpr int KK = (W + DR) / 32;       // score k-steps
   static constexpr int KKC = W / 32;             // k-steps over the latent part
   static constexpr int KKH = KK / CS;            // score k-steps of one wave
+  // absorbed-query row in the workspace: 4 W + 2 DR bytes; bf16 caches
+  // [hi (W) | lo (W) | q^R (DR)] in bf16, FP8 caches [fp16 (W) | q^R bf16 (DR) | 2^e fp32]
+  static constexpr int QWB = 4 * W + 2 * DR;
+  // registers for the lo parts of one head tile (bf16 caches): the wave's
+  // latent k-steps (the first KKC without column splits; with them the share
+  // depends on the wave's split)
+  static constexpr int NLO = F8 ? 1 : (CS > 1 ? KKH : KKC);
   static constexpr int NSUB = TT / 32;
   static constexpr int SUBW = NSUB / G;          // 32-token sub-tiles per wave per tile
   static constexpr int NQ = W / 128 / CS;        // 128-column groups per wave on the value side
@@ -124,6 +141,7 @@ struct Cfg {
   static_assert(PT_CAP >= 64, "LDS: room for the page-id table");
   static_assert(NTHREADS <= 1024, "");
   static_assert(HT % HPW == 0 && (HPW == 1 || CS == 1), "head tiles per wave: whole tiles, no column splits");
+  static_assert(!F8 || CS == 1, "FP8: the per-row query scale applies after the latent k-steps of one wave");
 };
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
@@ -144,8 +162,13 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __attribute__((address_space(4))) const int32_t cint32_t;
 __device__ __forceinline__ int32_t cload(const int32_t* p) { return *(cint32_t*)(p); }
 
-__device__ __forceinline__ floatx4_t mfma32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx4_t mfma_bf16(u32x4_t a, u32x4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_t mfma_f16(u32x4_t a, u32x4_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -178,6 +201,8 @@ __device__ __forceinline__ float sum_4lanes(float v) {
 // lgkmcnt before any LDS result can be used).
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 __device__ __forceinline__ u32x4_t gload16(const uint8_t* p) { return *(const gu32x4_t*)(p); }
+typedef __attribute__((address_space(1))) const float gfloat_t;
+__device__ __forceinline__ float gload4f(const uint8_t* p) { return *(const gfloat_t*)(p); }
 // The same load marked nontemporal, for the cache stream: every cache row is
 // read once per step, and the streaming hint lets HBM reads run measurably
 // closer to peak than plain loads do.
@@ -189,18 +214,20 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// 8 E4M3FN codes (8 bytes of LDS) -> 8 bf16 values (exact: E4M3 values are bf16 values)
+// 8 E4M3FN codes (8 bytes of LDS) -> 8 fp16 values (exact: E4M3 values are fp16 values)
 __device__ __forceinline__ u32x4_t widen8(const uint8_t* p) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t c = *reinterpret_cast<const u32x2_t*>(p);
   u32x4_t r;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h], 1.0f, false));
-    r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h], 1.0f, true));
+    r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[h], 1.0f, false));
+    r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[h], 1.0f, true));
   }
   return r;
 }
+
+constexpr int kNoExp = -100000;  // block scales: no running exponent yet
 
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_kernel(DecodeArgs a) {
@@ -336,6 +363,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   // ---- compute state
   floatx4_t O[HW][C::NQ][8];
   float m_run[HW], l_run[HW];
+  int e_run = kNoExp;  // block scales: the value side accumulates P s 2^-e_run
 #pragma unroll
   for (int hw = 0; hw < HW; ++hw) {
 #pragma unroll
@@ -345,7 +373,9 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
     m_run[hw] = -INFINITY;
     l_run[hw] = 0.f;
   }
-  bf16x8_t Qb[HW][C::KKH];  // this wave's score k-steps [cs KKH, (cs + 1) KKH), per head tile
+  u32x4_t Qb[HW][C::KKH];   // this wave's score k-steps [cs KKH, (cs + 1) KKH), per head tile
+  u32x4_t Ql[HW][C::NLO];   // bf16 caches: lo parts of its latent k-steps (zero for RoPE k-steps)
+  float qn[HW];             // FP8 caches: the row scale 2^e of the fp16 query
 
   int cb = lo;
   int32_t cb_start = pb_start, cb_end = pb_end, cb_n = pb_n;
@@ -353,20 +383,31 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   float* pm = reinterpret_cast<float*>(a.ws + a.off_pm);
   float* pl = reinterpret_cast<float*>(a.ws + a.off_pl);
   uint16_t* po = reinterpret_cast<uint16_t*>(a.ws + a.off_po);  // fp16 weighted latent sums
-  const uint16_t* qext = reinterpret_cast<const uint16_t*>(a.ws + a.off_qext);
+  const uint8_t* qext = reinterpret_cast<const uint8_t*>(a.ws + a.off_qext);
 
   auto load_q = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int hw = 0; hw < HW; ++hw) {
-      const uint16_t* qe = qext + (static_cast<int64_t>(b) * HK + hk[hw]) * (C::W + C::DR);
+      const uint8_t* qe = qext + (static_cast<int64_t>(b) * HK + hk[hw]) * C::QWB;
+      // byte offsets: latent parts, then the RoPE part after them
+      constexpr int kRope = C::F8 ? 2 * C::W : 4 * C::W;
 #pragma unroll
       for (int u = 0; u < C::KKH; ++u) {
         const int kk = cs * C::KKH + u;
-        const int off = kk < C::KKC ? 32 * kk + 8 * g4 : C::W + 32 * (kk - C::KKC) + 8 * g4;
+        const bool lat = kk < C::KKC;
+        const int off = lat ? 2 * (32 * kk + 8 * g4) : kRope + 2 * (32 * (kk - C::KKC) + 8 * g4);
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (head_ok[hw]) v = gload16(reinterpret_cast<const uint8_t*>(qe + off));
-        Qb[hw][u] = __builtin_bit_cast(bf16x8_t, v);
+        if (head_ok[hw]) v = gload16(qe + off);
+        Qb[hw][u] = v;
+        if constexpr (!C::F8) {
+          if (u < C::NLO) {
+            u32x4_t vl = u32x4_t{0u, 0u, 0u, 0u};
+            if (head_ok[hw] && lat) vl = gload16(qe + 2 * C::W + off);
+            Ql[hw][u] = vl;
+          }
+        }
       }
+      if constexpr (C::F8) qn[hw] = head_ok[hw] ? gload4f(qe + 2 * C::W + 2 * C::DR) : 1.f;
     }
   };
   load_q(cb);
@@ -398,14 +439,16 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   const int32_t nx_end = cload(ud + 6), nx_n = cload(ud + 7);  // the sequence after lo
   const int32_t ntab = (x1 - x0) * npt;
   if (ntab <= C::PT_CAP && x1 <= nx_end) {
-    // every tile of the unit lies in sequence lo or lo + 1
+    // every tile of the unit lies in sequence lo or lo + 1. lo's range comes
+    // from the compute cursor (cb_*), which still holds it: with the two-tile
+    // prologue the load cursor has already moved on when x0 is lo's last tile
     for (int i = tid; i < ntab; i += C::NTHREADS) {
       const int32_t x = x0 + i / npt;
       const int j = i % npt;
-      const bool first = x < pb_end;
+      const bool first = x < cb_end;
       const int b = first ? lo : lo + 1;
-      const int32_t start = first ? pb_start : pb_end;
-      const int32_t n = first ? pb_n : nx_n;
+      const int32_t start = first ? cb_start : cb_end;
+      const int32_t n = first ? cb_n : nx_n;
       const int32_t npg = (n + P - 1) >> a.log2_page;
       const int32_t pg0 = (((x - start) * C::TT) >> a.log2_page) + j;
       const int32_t pg = pg0 < npg ? pg0 : npg - 1;
@@ -541,18 +584,30 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         for (int u = 0; u < KB; ++u) {
           const int kl = kb + u;
           if (kl < C::KKH) {
+            const bool lat = cs * C::KKH + kl < C::KKC;
 #pragma unroll
             for (int hw = 0; hw < HW; ++hw) {
-              S0[hw] = mfma32(__builtin_bit_cast(bf16x8_t, A0[u]), Qb[hw][kl], S0[hw]);
-              S1[hw] = mfma32(__builtin_bit_cast(bf16x8_t, A1[u]), Qb[hw][kl], S1[hw]);
-              if constexpr (C::TS) {
+              if (C::F8 && lat) {
+                S0[hw] = mfma_f16(A0[u], Qb[hw][kl], S0[hw]);
+                S1[hw] = mfma_f16(A1[u], Qb[hw][kl], S1[hw]);
+              } else {
+                S0[hw] = mfma_bf16(A0[u], Qb[hw][kl], S0[hw]);
+                S1[hw] = mfma_bf16(A1[u], Qb[hw][kl], S1[hw]);
+              }
+              if constexpr (!C::F8) {
+                if (kl < C::NLO && lat) {
+                  S0[hw] = mfma_bf16(A0[u], Ql[hw][kl], S0[hw]);
+                  S1[hw] = mfma_bf16(A1[u], Ql[hw][kl], S1[hw]);
+                }
+              }
+              if constexpr (C::F8) {
                 if (kl == C::KKC - 1) {
-                  // the latent part is complete: scale it per token before the
-                  // RoPE k-steps add theirs
+                  // the latent part is complete: the query's row scale (and the
+                  // token's block scale) before the RoPE k-steps add theirs
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    S0[hw][i] *= sc0[i];
-                    S1[hw][i] *= sc1[i];
+                    S0[hw][i] *= C::TS ? qn[hw] * sc0[i] : qn[hw];
+                    S1[hw][i] *= C::TS ? qn[hw] * sc1[i] : qn[hw];
                   }
                 }
               }
@@ -580,6 +635,46 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           }
         }
       }
+      // base-2 logits: the query parts were not scaled by softmax_scale log2(e)
+#pragma unroll
+      for (int hw = 0; hw < HW; ++hw)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          S0[hw][i] *= a.qscale;
+          S1[hw][i] *= a.qscale;
+        }
+      // block scales: the value side takes P s 2^-e_run. e_run follows the
+      // largest scale of the sub-tile (the same for every lane: it depends on
+      // the tokens only); when that moves up, or more than 2^8 below, O is
+      // rescaled, so the fp16 weights of the sub-tile's largest terms keep
+      // their precision (s 2^-e_run < 1). A downward move is capped at 2^100
+      // so that O (at most ~2^20 in these units) stays finite.
+      int pexp = 0;  // P s is multiplied by 2^pexp
+      if constexpr (C::TS) {
+        float smax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) smax = fmaxf(smax, fmaxf(sc0[i], sc1[i]));
+        smax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(max_4lanes(smax))));
+        if (smax > 0.f && smax <= 3.0e38f) {
+          int et;
+          frexpf(smax, &et);  // smax < 2^et
+          if (e_run == kNoExp) {
+            e_run = et;  // O is still zero
+          } else if (et > e_run || et < e_run - 8) {
+            const int en = et > e_run ? et : max(et, e_run - 100);
+#pragma unroll
+            for (int hw = 0; hw < HW; ++hw)
+#pragma unroll
+              for (int q = 0; q < C::NQ; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) O[hw][q][e][i] = ldexpf(O[hw][q][e][i], e_run - en);
+            e_run = en;
+          }
+        }
+        if (e_run != kNoExp) pexp = -e_run;
+      }
       // value-side rows: 8 columns (col group 16 q' + m16 of the block, q' the
       // 128-column group) of 8 token rows
       auto read_rows = [&](int qg, u32x4_t* R) __attribute__((always_inline)) {
@@ -598,7 +693,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
       // the first 128-column group, read while the scores finish
       u32x4_t R[8];
       read_rows(cs * C::NQ, R);
-      bf16x8_t pb[HW];
+      u32x4_t pb[HW];
 #pragma unroll
       for (int hw = 0; hw < HW; ++hw) {
         if (valid < C::TT) {
@@ -636,13 +731,16 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
           // softmax sum above keeps the unscaled p_t
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p0[i] *= sc0[i];
-            p1[i] *= sc1[i];
+            p0[i] *= ldexpf(sc0[i], pexp);
+            p1[i] *= ldexpf(sc1[i], pexp);
           }
         }
-        const u32x4_t pbu = u32x4_t{pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
-                                    pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
-        pb[hw] = __builtin_bit_cast(bf16x8_t, pbu);
+        if constexpr (C::F8)
+          pb[hw] = u32x4_t{pack_f16x2(p0[0], p0[1]), pack_f16x2(p0[2], p0[3]), pack_f16x2(p1[0], p1[1]),
+                           pack_f16x2(p1[2], p1[3])};
+        else
+          pb[hw] = u32x4_t{pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]), pack_bf16x2(p1[0], p1[1]),
+                           pack_bf16x2(p1[2], p1[3])};
       }
       // ---- values: O^T[col][head] += C^T[col][tokens] P^T[tokens][head]
 #pragma unroll
@@ -657,7 +755,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
             Av[u] = __builtin_amdgcn_perm(R[2 * u + 1][e >> 1], R[2 * u][e >> 1], sel);
 #pragma unroll
           for (int hw = 0; hw < HW; ++hw)
-            O[hw][q][e] = mfma32(__builtin_bit_cast(bf16x8_t, Av), pb[hw], O[hw][q][e]);
+            O[hw][q][e] = C::F8 ? mfma_f16(Av, pb[hw], O[hw][q][e]) : mfma_bf16(Av, pb[hw], O[hw][q][e]);
         }
       }
     }
@@ -705,8 +803,11 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
               *reinterpret_cast<u32x4_t*>(dst + 128 * (cs * C::NQ + q) + 8 * (4 * g4 + i)) = v;
             }
           if (g4 == 0 && cs == 0) {
-            pm[slot * HK + hk[hw]] = m_run[hw] + static_cast<float>(sexp);
-            pl[slot * HK + hk[hw]] = l_tot * rs;
+            // block scales: the sums are O 2^e_run, so the stored row's scale
+            // exponent is sexp + e_run
+            const int tot = C::TS && e_run != kNoExp ? sexp + e_run : sexp;
+            pm[slot * HK + hk[hw]] = m_run[hw] + static_cast<float>(tot);
+            pl[slot * HK + hk[hw]] = ldexpf(l_tot, -tot);
           }
         }
 #pragma unroll
@@ -716,6 +817,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         m_run[hw] = -INFINITY;
         l_run[hw] = 0.f;
       }
+      e_run = kNoExp;
     }
     if constexpr (C::CF) {
       // tile x+1 has been in flight since the previous step; its buffer was

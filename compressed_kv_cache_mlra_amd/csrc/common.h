@@ -10,7 +10,13 @@ namespace mlra {
 //   [0, 256)     WsHeader
 //   cum          int32 [batch + 1]  prefix sums of tiles per sequence
 //   nlen         int32 [batch]      clamped sequence lengths
-//   qext         [batch][hk][w + d_r]  absorbed queries (bf16 or fp32), base-2 scaled
+//   qext         [batch][hk] rows of absorbed queries, by query mode (DecodeArgs::q_mode):
+//                  kQueryF32   fp32 [w + d_r], latent and RoPE parts scaled by softmax_scale log2(e)
+//                  kQuerySplit bf16 [hi (w) | lo (w) | q^R (d_r)]: the latent part v = W^UK^T q^C
+//                              as v = hi + lo (about 16 significant bits), q^R as given; not scaled
+//                  kQueryF16   [v 2^-e as fp16 (w) | q^R bf16 (d_r) | 2^e fp32], e chosen per row
+//                              so the largest |v 2^-e| is in [1, 2); not scaled by softmax_scale
+//                the two MFMA modes use 4 w + 2 d_r bytes per row
 //   pm, pl       fp32 [slots][hk]      partial running max / sum
 //   po           fp32 [slots][hk][w]   partial weighted latent sums
 // hk = n_heads * blocks_per_head; slots = (units + batch) * groups + 1 (the
@@ -35,6 +41,8 @@ constexpr int kMaxBatch = 4096;             // sequences per call (the plan keep
 // lo owning x0, 3 cum[lo], 4 cum[lo + 1], 5 length of lo, 6 cum[lo + 2] (the
 // tile count when lo is the last sequence), 7 length of lo + 1 (0 if none).
 constexpr int kUnitDescInts = 8;
+// Absorbed-query layouts (qext rows, above).
+constexpr int kQueryF32 = 0, kQuerySplit = 1, kQueryF16 = 2;
 
 // Everything a decode kernel needs, passed by value.
 struct DecodeArgs {
@@ -44,6 +52,8 @@ struct DecodeArgs {
   int64_t off_cum, off_nlen, off_sunit, off_udesc, off_qext, off_pm, off_pl, off_po;
   int32_t po_f16;     // weighted latent sums of the partials stored as fp16 rows scaled by a
                       // power of two folded into m and l (MFMA path), else fp32
+  int32_t q_mode;     // absorbed-query layout: kQueryF32 (generic path), kQuerySplit (bf16
+                      // caches on MFMA) or kQueryF16 (FP8 caches on MFMA)
   int32_t batch;
   int32_t n_heads;
   int32_t d_h;

@@ -34,6 +34,11 @@ per latent block after the RoPE key, then zero bytes up to a multiple of 16.
 Step 3 draws the codes and RoPE key as for "fp8", then each scale as
 2^u, u uniform in [-3, 1) (fp32), so scales differ by up to 16x between tokens
 and blocks. Canary rows hold NaN scales.
+
+make_inputs(fp8_codes="full") instead draws every latent code uniformly from
+all 254 finite E4M3FN codes (zero, both signed zeros, the subnormals 0x01..0x07
+and the largest magnitude 448, code 0x7E), and scale_exp=(lo, hi) sets the
+range of u for block scales.
 """
 from __future__ import annotations
 
@@ -148,6 +153,12 @@ WORKLOADS = {
                   "d_r=64 ctx=8192 paged",
              shape=Shape(batch=32, n_heads=24, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16", blocks_per_head=4),
              lengths=("fixed", 8192)),
+    # one rank's share of MLRA-2 under 2-way tensor parallelism: one 256-wide
+    # latent block and the RoPE key serving its 32 query heads, at the batch and
+    # context of the MLRA-4 share above
+    13: dict(name="MLRA-2 one TP-2 rank share, bf16, B=64 h=32 d_h=128 d_c=256 d_r=64 ctx=32768 paged",
+             shape=Shape(batch=64, n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"),
+             lengths=("fixed", 32768)),
 }
 
 
@@ -203,24 +214,31 @@ class Inputs:
         return int(self.seq_lens.max()) if self.seq_lens.size else 0
 
 
-def _fp8_pool(rng: np.random.Generator, pages_rows, d_c: int, d_r: int) -> np.ndarray:
+def _fp8_pool(rng: np.random.Generator, pages_rows, d_c: int, d_r: int, codes: str = "narrow") -> np.ndarray:
     """FP8 cache rows: E4M3FN code fields drawn as integers, then the bf16 RoPE key."""
     size = tuple(pages_rows) + (d_c,)
-    sign = rng.integers(0, 2, size=size, dtype=np.uint8)
-    expo = rng.integers(3, 8, size=size, dtype=np.uint8)
-    mant = rng.integers(0, 8, size=size, dtype=np.uint8)
+    if codes == "full":
+        # every finite code: 0x00..0x7E and 0x80..0xFE (0x7F and 0xFF are NaN)
+        v = rng.integers(0, 254, size=size, dtype=np.int32)
+        lat = np.where(v < 127, v, v + 1).astype(np.uint8)
+    else:
+        sign = rng.integers(0, 2, size=size, dtype=np.uint8)
+        expo = rng.integers(3, 8, size=size, dtype=np.uint8)
+        mant = rng.integers(0, 8, size=size, dtype=np.uint8)
+        lat = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
     rope = _normal(rng, tuple(pages_rows) + (d_r,), 1.0, "bf16")
     pool = np.empty(tuple(pages_rows) + (d_c + 2 * d_r,), dtype=np.uint8)
-    pool[..., :d_c] = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
+    pool[..., :d_c] = lat
     pool[..., d_c:] = rope.view(np.uint8).reshape(tuple(pages_rows) + (2 * d_r,))
     return pool
 
 
-def _fp8b_pool(rng: np.random.Generator, pages_rows, shape: "Shape") -> np.ndarray:
+def _fp8b_pool(rng: np.random.Generator, pages_rows, shape: "Shape", codes: str = "narrow",
+               scale_exp=(-3.0, 1.0)) -> np.ndarray:
     """Block-scaled FP8 rows: the fp8 row, n_blocks fp32 scales 2^u, zero pad."""
     d_c, d_r, nb = shape.d_c, shape.d_r, shape.n_blocks
-    base = _fp8_pool(rng, pages_rows, d_c, d_r)
-    u = rng.uniform(-3.0, 1.0, size=tuple(pages_rows) + (nb,))
+    base = _fp8_pool(rng, pages_rows, d_c, d_r, codes)
+    u = rng.uniform(float(scale_exp[0]), float(scale_exp[1]), size=tuple(pages_rows) + (nb,))
     scales = np.exp2(u).astype(np.float32)
     pool = np.zeros(tuple(pages_rows) + (shape.row_bytes,), dtype=np.uint8)
     pool[..., :d_c + 2 * d_r] = base
@@ -244,7 +262,7 @@ def _normal(rng: np.random.Generator, shape, scale: float, dtype: str) -> np.nda
 
 
 def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
-                pool_copies: int = 1) -> Inputs:
+                pool_copies: int = 1, fp8_codes: str = "narrow", scale_exp=(-3.0, 1.0)) -> Inputs:
     """Draws one workload.
 
     lengths: ("fixed", n) | ("uniform", lo, hi) | ("uniform_append", lo, hi) |
@@ -253,6 +271,8 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
     slot L_b and the decode attends n_b = L_b + 1 tokens.
     pool_copies > 1 returns a list of independent pools in Inputs.pool (same
     page table), for benchmarks that rotate cache instances.
+    fp8_codes ("narrow" | "full") and scale_exp: FP8 code and block-scale
+    draws (module docstring).
     """
     rng = np.random.Generator(np.random.Philox(seed))
     B, P = shape.batch, shape.page_size
@@ -294,10 +314,10 @@ def make_inputs(shape: Shape, lengths, seed: int, canary: bool = True,
     pools = []
     for _ in range(pool_copies):
         if shape.dtype == "fp8":
-            pool = _fp8_pool(rng, (n_pages, P), shape.d_c, shape.d_r)
+            pool = _fp8_pool(rng, (n_pages, P), shape.d_c, shape.d_r, fp8_codes)
             nanv = _FP8_NAN_ROW(shape.d_c, shape.d_r)
         elif shape.dtype == "fp8b":
-            pool = _fp8b_pool(rng, (n_pages, P), shape)
+            pool = _fp8b_pool(rng, (n_pages, P), shape, fp8_codes, scale_exp)
             nanv = _FP8_NAN_ROW(shape.d_c, shape.d_r, shape.row_bytes, shape.n_blocks)
         else:
             pool = _normal(rng, (n_pages, P, row), 1.0, shape.dtype)

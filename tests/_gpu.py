@@ -84,23 +84,19 @@ def rms(a):
 
 
 def check_outputs(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "out"):
-    """bf16: max |g - r| / RMS(r) <= 2e-2; fp8 caches: <= 3e-2 (block-scaled: 5e-2);
-    fp32: max |g - r| / max(|r|, RMS(r)) <= 1e-5."""
+    """bf16 and FP8 caches: max |g - r| / RMS(r) <= 2e-2, the RMS taken over
+    every output compared; fp32: max |g - r| / max(|r|, RMS(r)) <= 1e-5.
+
+    The FP8 bar equals the bf16 one, fixed before any run: the oracle decodes
+    the same E4M3 codes exactly, and the FP8 kernels round less than the bf16
+    ones (fp16 query and weights P, 11 significant bits, against the bf16
+    path's P at 8 bits; a 16-bit query on both)."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
     r = rms(ref)
     if dtype in ("bf16", "fp8", "fp8b"):
-        # fp8 caches (either scaling) compute exactly like the bf16 path (bf16 q~ and P, fp32
-        # accumulation); their bar is what those two roundings produce on the
-        # fp8 test inputs: a numpy emulation of just those roundings reaches
-        # 2.7e-2 of the RMS on the worst case, so the bar is 3e-2
-        # block-scaled caches (scales up to 2 per token and block) widen the
-        # logits, so the q~ rounding weighs more: the same emulation, with p s
-        # rounded to bf16, reaches 3.8e-2 and 4.0e-2 of the sequence RMS on the
-        # MLRA-2 test inputs, so their bar is 5e-2
-        tol = {"bf16": 2e-2, "fp8": 3e-2, "fp8b": 5e-2}[dtype]
         err = float(np.max(np.abs(gpu - ref))) / max(r, 1e-30)
-        assert err <= tol, f"{what}: max err / rms = {err:.3e}"
+        assert err <= 2e-2, f"{what}: max err / rms = {err:.3e}"
     else:
         err = float(np.max(np.abs(gpu - ref) / np.maximum(np.abs(ref), r)))
         assert err <= 1e-5, f"{what}: max rel err = {err:.3e}"
@@ -115,3 +111,30 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, dtype: str):
         d = np.abs(gpu[finite] - ref[finite])
         tol = 5e-2 if dtype in ("bf16", "fp8", "fp8b") else 1e-5 * max(1.0, float(np.max(np.abs(ref[finite]))))
         assert float(np.max(d)) <= tol, f"lse: max abs err {float(np.max(d)):.3e}"
+
+
+def plan_geometry(shape: "synth.Shape"):
+    """(work units, tokens per tile) of the attention launch for this shape on
+    the current device, read from the workspace header after planning a
+    single long sequence (header: magic, flags, tiles, units, tile tokens)."""
+    t = torch()
+    s = synth.Shape(**{**shape.__dict__, "batch": 1, "d_model": 0, "d_cq": 0})
+    n = 1 << 20
+    desc = mlra.make_desc(batch=1, n_heads=s.n_heads, d_h=s.d_h, d_c=s.d_c, n_blocks=s.n_blocks, d_r=s.d_r,
+                          max_pages_per_seq=n // s.page_size, num_pages=1, dtype=s.dtype, page_size=s.page_size,
+                          blocks_per_head=s.blocks_per_head, cache_scale=s.cache_scale)
+    ws = mlra.alloc_workspace(desc, n)
+    et = t.float32 if s.dtype == "f32" else t.bfloat16
+    q_c = t.zeros((1, s.n_heads, s.d_h), dtype=et, device="cuda")
+    q_r = t.zeros((1, s.n_heads, max(s.d_r, 1)), dtype=et, device="cuda")
+    w_uk = t.zeros((s.n_heads, s.blocks_per_head, s.w, s.d_h), dtype=et, device="cuda")
+    lens = t.tensor([n], dtype=t.int32, device="cuda")
+    mlra.absorb_query(desc, lens, q_c, q_r, w_uk, ws)
+    t.cuda.synchronize()
+    hdr = ws[:32].cpu().numpy().view(np.int32)
+    return int(hdr[3]), int(hdr[4])
+
+
+def tile_begin(u: int, n_tiles: int, units: int) -> int:
+    """First tile of work unit u (the plan's balanced split)."""
+    return (u * n_tiles) // units

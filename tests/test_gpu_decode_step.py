@@ -51,14 +51,11 @@ def test_step_equals_separate_calls_and_oracle(name):
     ref, rl = oracle.decode_unabsorbed(inp, pairs)
     g = np.stack([out[b, i] for b, i in pairs])
     _gpu.check_lse(np.stack([lse[b, i] for b, i in pairs]), rl, s.dtype)
-    worst = 0.0
-    for b in range(s.batch):
-        rows = [k for k, (bb, _) in enumerate(pairs) if bb == b]
+    for k, (b, _) in enumerate(pairs):
         if LENS[b] == 0:
-            assert np.all(g[rows] == 0)
-            continue
-        worst = max(worst, _gpu.check_outputs(g[rows], ref[rows], s.dtype, f"sequence {b}"))
-    _say(f"  max err / sequence rms {worst:.2e}")
+            assert np.all(g[k] == 0)
+    worst = _gpu.check_outputs(g, ref, s.dtype)
+    _say(f"  max err / rms {worst:.2e}")
 
 
 def test_repeated_steps_with_changing_lengths():
@@ -93,7 +90,7 @@ def test_full_size_mlra4_step():
     s = inp.shape
     rng = np.random.default_rng(2)
     pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
-    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
+    pairs += [(s.batch // 2, i) for i in range(s.n_heads)]
     ref, rl = oracle.decode_unabsorbed(inp, pairs)
     err = _gpu.check_outputs(np.stack([out[b, i] for b, i in pairs]), ref, "bf16")
     _gpu.check_lse(np.stack([lse[b, i] for b, i in pairs]), rl, "bf16")

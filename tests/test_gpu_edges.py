@@ -16,17 +16,15 @@ def _say(msg):
 
 
 def _check_pairs(inp, out, lse, pairs):
+    """Outputs against the oracle on one RMS over every compared output;
+    empty sequences must give exactly 0."""
     ref, rl = oracle.decode_unabsorbed(inp, pairs)
     g = np.stack([out[b, i] for b, i in pairs])
     _gpu.check_lse(np.stack([lse[b, i] for b, i in pairs]), rl, inp.shape.dtype)
-    worst = 0.0
-    for b in sorted({b for b, _ in pairs}):
-        rows = [k for k, (bb, _) in enumerate(pairs) if bb == b]
-        if int(inp.seq_lens[b]) == 0:
-            assert np.all(g[rows] == 0), f"sequence {b} is empty but has non-zero outputs"
-            continue
-        worst = max(worst, _gpu.check_outputs(g[rows], ref[rows], inp.shape.dtype, f"sequence {b}"))
-    return worst
+    for k, (b, _) in enumerate(pairs):
+        if int(inp.seq_lens[b]) <= 0:
+            assert np.all(g[k] == 0), f"sequence {b} is empty but has non-zero outputs"
+    return _gpu.check_outputs(g, ref, inp.shape.dtype)
 
 
 def test_largest_batch():
@@ -47,7 +45,7 @@ def test_largest_batch():
     worst = _check_pairs(inp, out, lse, pairs)
     out2, lse2 = prob.run(one_call=True)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
-    _say(f"  max err / sequence rms {worst:.2e}")
+    _say(f"  max err / rms {worst:.2e}")
 
 
 def test_lengths_outside_capacity_are_clamped():
@@ -79,7 +77,7 @@ def test_head_widths(d_h):
     out, lse = prob.run()
     pairs = [(b, i) for b in range(s.batch) for i in range(s.n_heads)]
     worst = _check_pairs(inp, out, lse, pairs)
-    _say(f"  max err / sequence rms {worst:.2e}")
+    _say(f"  max err / rms {worst:.2e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

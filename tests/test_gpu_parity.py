@@ -1,16 +1,18 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Small cases compare every output element; the five full-size workloads (in
-the launch configuration the benchmark times) compare sampled (b, head)
-outputs that the oracle computes one by one. Tolerances: fp32 max relative
-error 1e-5 (floor: output RMS), bf16 max error 2e-2 of the output RMS,
-indexing and page-permutation results bit-exact.
+Small cases compare every output element; the full-size workloads (in the
+launch configuration the benchmark times) compare every head of the first and
+last sequence (workload 5: the longest and the shortest) plus sampled pairs,
+which the oracle computes one by one. Tolerances: fp32 max relative error 1e-5
+(floor: output RMS); bf16 and FP8 caches max error 2e-2 of the RMS of all
+outputs compared; indexing and page-permutation results bit-exact.
 """
 import sys
 
 import numpy as np
 import pytest
 
+import compressed_kv_cache_mlra_amd as mlra
 import oracle
 import synth
 from tests import _gpu
@@ -23,6 +25,8 @@ SMALL = {
     3: (dict(n_heads=64, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="bf16"), [31, 96, 200]),
     4: (dict(n_heads=16, d_h=128, d_c=128, n_blocks=1, d_r=64, dtype="bf16"), [5, 128, 129, 900, 2049]),
     5: (dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="bf16"), [100, 0, 333]),
+    # the TP-2 share of MLRA-2: one 256-wide block serving 32 heads
+    13: (dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"), [7, 64, 65, 1000, 3001]),
 }
 
 
@@ -31,30 +35,36 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run_and_compare(inp, pairs=None, lse=True, per_sequence=False):
-    """per_sequence: each sequence's outputs against that sequence's own RMS
-    (ragged batches, where a short sequence's outputs are many times larger)."""
+def _compare(inp, out, l, pairs, lse=True):
+    """Outputs of (b, head) pairs against the oracle on one batch-wide RMS;
+    empty sequences must give exactly 0."""
+    s = inp.shape
+    ref, rl = oracle.decode_unabsorbed(inp, pairs)
+    g = np.stack([out[b, i] for b, i in pairs])
+    for k, (b, _) in enumerate(pairs):
+        if int(inp.seq_lens[b]) <= 0:
+            assert np.all(g[k] == 0), f"sequence {b} is empty but has non-zero outputs"
+    err = _gpu.check_outputs(g, ref, s.dtype)
+    if lse:
+        _gpu.check_lse(np.stack([l[b, i] for b, i in pairs]), rl, s.dtype)
+    return err
+
+
+def _run_and_compare(inp, pairs=None, lse=True):
     prob = _gpu.GpuProblem(inp)
     out, l = prob.run()
     s = inp.shape
     if pairs is None:
         pairs = [(b, i) for b in range(s.batch) for i in range(s.n_heads)]
-    ref, rl = oracle.decode_unabsorbed(inp, pairs)
-    g = np.stack([out[b, i] for b, i in pairs])
-    gl = np.stack([l[b, i] for b, i in pairs])
-    if per_sequence:
-        err = 0.0
-        for b in sorted({b for b, _ in pairs}):
-            rows = [k for k, (bb, _) in enumerate(pairs) if bb == b]
-            if int(inp.seq_lens[b]) == 0:
-                assert np.all(g[rows] == 0)
-                continue
-            err = max(err, _gpu.check_outputs(g[rows], ref[rows], s.dtype, f"sequence {b}"))
-    else:
-        err = _gpu.check_outputs(g, ref, s.dtype)
-    if lse:
-        _gpu.check_lse(gl, rl, s.dtype)
-    return prob, err
+    return prob, _compare(inp, out, l, pairs, lse)
+
+
+def _first_last_pairs(s, seed, extra=6):
+    """Every head of the first and the last sequence, plus random pairs."""
+    rng = np.random.default_rng(seed)
+    pairs = [(b, i) for b in (0, s.batch - 1) for i in range(s.n_heads)]
+    pairs += [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(extra)]
+    return pairs
 
 
 def test_workload1_full_fp32():
@@ -65,7 +75,7 @@ def test_workload1_full_fp32():
     _say(f"workload 1 max rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("wl", [2, 3, 4, 5])
+@pytest.mark.parametrize("wl", [2, 3, 4, 5, 13])
 def test_small_all_outputs(wl):
     kw, lens = SMALL[wl]
     _say(f"case: small shape of workload {wl}, lengths {lens}")
@@ -75,28 +85,32 @@ def test_small_all_outputs(wl):
     _say(f"workload {wl} small: max err/rms {err:.2e}")
 
 
-@pytest.mark.parametrize("wl", [2, 3, 4])
-def test_full_size_sampled(wl):
+@pytest.mark.parametrize("wl", [2, 3, 4, 13])
+def test_full_size_first_last_all_heads(wl):
+    """Full-size workloads as the benchmark launches them: every head of the
+    first and the last sequence, and sampled pairs, against the oracle."""
     _say(f"case: full-size workload {wl}")
     inp = synth.workload_inputs(wl)
-    rng = np.random.default_rng(wl)
-    s = inp.shape
-    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
-    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
-    _, err = _run_and_compare(inp, pairs)
+    prob = _gpu.GpuProblem(inp)
+    out, l = prob.run()
+    assert mlra.read_flags(prob.ws) == 0
+    err = _compare(inp, out, l, _first_last_pairs(inp.shape, wl))
     _say(f"workload {wl} full: max err/rms {err:.2e}")
 
 
 def test_full_size_workload5_with_append():
-    """Ragged MLRA-2 with the latent append of one token per sequence."""
+    """Ragged MLRA-2 with the latent append of one token per sequence: the
+    append bit for bit, then every head of the longest and the shortest
+    sequence (the longest spans the most work units) against the oracle."""
     _say("case: full-size workload 5 (append + ragged decode)")
     inp = synth.workload_inputs(5)
     prob = _gpu.GpuProblem(inp)
     prob.append()
     out, l = prob.run()
+    assert mlra.read_flags(prob.ws) == 0
     pool_after = _gpu.from_dev_bits(prob.pool)
     c_gpu = _gpu.from_dev_bits(prob.c_out)
-    # oracle append on the host copy, then sampled decode on the appended pool
+    # oracle append on the host copy, then the decode on the appended pool
     pool_ref = inp.pool.copy()
     c_ref = oracle.append(inp, pool_ref)
     ulp = np.abs(c_gpu.astype(np.int32) - c_ref.astype(np.int32))
@@ -108,13 +122,12 @@ def test_full_size_workload5_with_append():
         assert np.array_equal(pool_after[pg, off, :s.d_c], c_gpu[b])
         assert np.array_equal(pool_after[pg, off, s.d_c:], inp.kr_new[b])
     inp.pool = pool_after  # decode parity on the GPU's own appended cache
-    rng = np.random.default_rng(5)
-    short = np.argsort(inp.seq_lens)[:4]
-    pairs = [(int(b), int(rng.integers(s.n_heads))) for b in short] + [(int(short[0]), 0)]
-    ref, rl = oracle.decode_unabsorbed(inp, pairs)
-    g = np.stack([out[b, i] for b, i in pairs])
-    err = _gpu.check_outputs(g, ref, "bf16")
-    _gpu.check_lse(np.stack([l[b, i] for b, i in pairs]), rl, "bf16")
+    order = np.argsort(inp.seq_lens)
+    longest, shortest = int(order[-1]), int(order[0])
+    _say(f"  longest sequence {longest}: {int(inp.seq_lens[longest])} tokens, "
+         f"shortest {shortest}: {int(inp.seq_lens[shortest])}")
+    pairs = [(b, i) for b in (longest, shortest) for i in range(s.n_heads)]
+    err = _compare(inp, out, l, pairs)
     _say(f"workload 5 full: max err/rms {err:.2e}")
 
 
@@ -133,32 +146,31 @@ def test_append_exact_and_canary(kw):
     """Append writes exactly the target rows; every other pool byte is unchanged."""
     _say(f"case: append exactness {kw}")
     dtype = kw["dtype"]
-    if True:
-        s = synth.Shape(batch=5, **kw)
-        inp = synth.make_inputs(s, ("list_append", [0, 63, 64, 127, 500]), 77)
-        prob = _gpu.GpuProblem(inp)
-        before = _gpu.from_dev_bits(prob.pool).copy()
-        prob.append()
-        after = _gpu.from_dev_bits(prob.pool)
-        c_gpu = _gpu.from_dev_bits(prob.c_out)
-        pool_ref = inp.pool.copy()
-        c_ref = oracle.append(inp, pool_ref)
-        if dtype == "bf16":
-            d = np.abs(c_gpu.astype(np.int32) - c_ref.astype(np.int32))
-            assert d.max() <= 1
-        else:
-            err = np.abs(c_gpu.astype(np.float64) - c_ref) / np.maximum(np.abs(c_ref), _gpu.rms(c_ref))
-            assert err.max() <= 1e-5, err.max()
-        changed = np.zeros(before.shape[:2], dtype=bool)
-        for b in range(s.batch):
-            pos = int(inp.positions[b])
-            pg, off = inp.page_table[b, pos // 64], pos % 64
-            changed[pg, off] = True
-            assert np.array_equal(after[pg, off, :s.d_c], c_gpu[b])
-            assert np.array_equal(after[pg, off, s.d_c:], inp.kr_new[b])
-        bv = before.view(np.uint16 if dtype == "bf16" else np.uint32)
-        av = after.view(bv.dtype)
-        assert np.array_equal(bv[~changed], av[~changed])
+    s = synth.Shape(batch=5, **kw)
+    inp = synth.make_inputs(s, ("list_append", [0, 63, 64, 127, 500]), 77)
+    prob = _gpu.GpuProblem(inp)
+    before = _gpu.from_dev_bits(prob.pool).copy()
+    prob.append()
+    after = _gpu.from_dev_bits(prob.pool)
+    c_gpu = _gpu.from_dev_bits(prob.c_out)
+    pool_ref = inp.pool.copy()
+    c_ref = oracle.append(inp, pool_ref)
+    if dtype == "bf16":
+        d = np.abs(c_gpu.astype(np.int32) - c_ref.astype(np.int32))
+        assert d.max() <= 1
+    else:
+        err = np.abs(c_gpu.astype(np.float64) - c_ref) / np.maximum(np.abs(c_ref), _gpu.rms(c_ref))
+        assert err.max() <= 1e-5, err.max()
+    changed = np.zeros(before.shape[:2], dtype=bool)
+    for b in range(s.batch):
+        pos = int(inp.positions[b])
+        pg, off = inp.page_table[b, pos // 64], pos % 64
+        changed[pg, off] = True
+        assert np.array_equal(after[pg, off, :s.d_c], c_gpu[b])
+        assert np.array_equal(after[pg, off, s.d_c:], inp.kr_new[b])
+    bv = before.view(np.uint16 if dtype == "bf16" else np.uint32)
+    av = after.view(bv.dtype)
+    assert np.array_equal(bv[~changed], av[~changed])
 
 
 def test_page_permutation_bit_exact():
@@ -230,7 +242,6 @@ def test_bad_page_id_is_flagged_not_dereferenced():
     inp.page_table[1, 1] = 10 ** 6
     prob = _gpu.GpuProblem(inp)
     out, _ = prob.run()
-    import compressed_kv_cache_mlra_amd as mlra
     assert mlra.read_flags(prob.ws) & mlra.FLAG_BAD_PAGE
     # the sequence with valid pages is unaffected
     ref, _ = oracle.decode_unabsorbed(inp, [(0, i) for i in range(64)])
@@ -286,19 +297,16 @@ def test_graph_replay_matches_eager():
         t.cuda.synchronize()
 
 
-
 @pytest.mark.parametrize("wl", [9, 10, 11, 12])
-def test_reading_b_and_h24_full_size_sampled(wl):
+def test_reading_b_and_h24_full_size(wl):
     """Reading B (k = 2, 4) and the 24-head width at full size (B = 32, 8192
-    tokens, the launches bench.py times): sampled (sequence, head) pairs,
-    including the last head, against the oracle; outputs and every block's lse."""
+    tokens, the launches bench.py times): every head of the first and the last
+    sequence and sampled pairs against the oracle; outputs and every block's lse."""
     _say(f"case: full-size workload {wl}")
     inp = synth.workload_inputs(wl)
-    s = inp.shape
-    rng = np.random.default_rng(wl)
-    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
-    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
-    _, err = _run_and_compare(inp, pairs)
+    prob = _gpu.GpuProblem(inp)
+    out, l = prob.run()
+    err = _compare(inp, out, l, _first_last_pairs(inp.shape, wl))
     _say(f"workload {wl} full: max err/rms {err:.2e}")
 
 
@@ -328,15 +336,37 @@ def test_fp8_small_all_outputs(name):
     _say(f"fp8 {name}: max err/rms {err:.2e}")
 
 
-def test_fp8_full_size_sampled():
-    _say("case: full-size fp8 workload (MLRA-4 shape, B=32, 8K)")
-    inp = synth.workload_inputs(6)
-    rng = np.random.default_rng(6)
-    s = inp.shape
-    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
-    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
-    _, err = _run_and_compare(inp, pairs)
-    _say(f"fp8 full: max err/rms {err:.2e}")
+@pytest.mark.parametrize("dtype", ["fp8", "fp8b"])
+@pytest.mark.parametrize("name", list(FP8_SHAPES))
+def test_fp8_full_code_range(name, dtype):
+    """Every finite E4M3FN code (zeros, subnormals, up to 448) in the latent,
+    and for block-scaled caches scales 2^u with u in [-8, 8): every output
+    against the oracle. The softmax scale is lowered so that the logits stay
+    of order one over such latents (the parity bar is relative to the output
+    RMS either way)."""
+    kw, lens = FP8_SHAPES[name]
+    kw = dict(kw, dtype=dtype)
+    if dtype == "fp8b":
+        kw.pop("cache_scale")
+        kw["softmax_scale"] = 2e-5
+    else:
+        kw["cache_scale"] = 2.0 ** -7
+        kw["softmax_scale"] = 0.05
+    _say(f"case: fp8 full code range {name} {dtype}, lengths {lens}")
+    s = synth.Shape(batch=len(lens), **kw)
+    inp = synth.make_inputs(s, ("list", lens), 4400 + len(name), fp8_codes="full", scale_exp=(-8.0, 8.0))
+    _, err = _run_and_compare(inp)
+    _say(f"  max err/rms {err:.2e}")
+
+
+@pytest.mark.parametrize("wl", [6, 8])
+def test_fp8_full_size_first_last_all_heads(wl):
+    _say(f"case: full-size fp8 workload {wl} (MLRA-4 shape, B=32, 8K)")
+    inp = synth.workload_inputs(wl)
+    prob = _gpu.GpuProblem(inp)
+    out, l = prob.run()
+    err = _compare(inp, out, l, _first_last_pairs(inp.shape, wl))
+    _say(f"fp8 workload {wl} full: max err/rms {err:.2e}")
 
 
 def test_fp8_append_encodes_kernel_latent():
@@ -374,29 +404,15 @@ def test_fp8_append_encodes_kernel_latent():
 def test_fp8b_small_all_outputs(name):
     """Block-scaled FP8 caches (scales 2^u, u in [-3, 1), per token and block;
     NaN codes, keys and scales in unused rows) against the oracle on every
-    output and lse, for each of the four kernel shapes. Sequence by sequence:
-    p_t s_t is rounded to bf16 even for a one-token sequence (a power-of-two
-    cache scale made that exact), and such a sequence's outputs are many times
-    the batch RMS."""
+    output and lse, for each of the four kernel shapes."""
     kw, lens = FP8_SHAPES[name]
     kw = dict(kw, dtype="fp8b")
     kw.pop("cache_scale")
     _say(f"case: fp8b {name}, lengths {lens}")
     s = synth.Shape(batch=len(lens), **kw)
     inp = synth.make_inputs(s, ("list", lens), 4300 + len(name))
-    _, err = _run_and_compare(inp, per_sequence=True)
+    _, err = _run_and_compare(inp)
     _say(f"fp8b {name}: max err/rms {err:.2e}")
-
-
-def test_fp8b_full_size_sampled():
-    _say("case: full-size fp8b workload (MLRA-4 shape, B=32, 8K)")
-    inp = synth.workload_inputs(8)
-    rng = np.random.default_rng(8)
-    s = inp.shape
-    pairs = [(int(rng.integers(s.batch)), int(rng.integers(s.n_heads))) for _ in range(6)]
-    pairs += [(0, 0), (s.batch - 1, s.n_heads - 1)]
-    _, err = _run_and_compare(inp, pairs)
-    _say(f"fp8b full: max err/rms {err:.2e}")
 
 
 def test_fp8b_append_encodes_each_block():
@@ -433,53 +449,93 @@ def test_fp8b_append_encodes_each_block():
     assert np.array_equal(before[~changed], after[~changed])
 
 
-# The tuned kernel of each configured shape (step order, two-tile prologue and
-# column splits differ between them), on inputs that stress the unit plan:
-# many short and empty sequences, so work units span several sequences (the
-# prologue's page-id gather falls back beyond two), and pages smaller than a
-# tile.
+# ---------------------------------------------- every tuned attention variant
+
+# One shape per tuned kernel (step order, two-tile prologue, column splits,
+# head tiles per wave and tile size differ between them).
+_MLRA4 = dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64)
+_MLA = dict(_MLRA4, n_blocks=1)
+_TP4 = dict(n_heads=16, d_h=128, d_c=128, n_blocks=1, d_r=64)
+_MLRA2 = dict(_MLRA4, n_blocks=2)
 VARIANT_SHAPES = {
-    "mlra4": dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16"),
-    "mla": dict(n_heads=64, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="bf16"),
-    "tp-share": dict(n_heads=16, d_h=128, d_c=128, n_blocks=1, d_r=64, dtype="bf16"),
-    "mlra2": dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="bf16"),
-    "mlra4-fp8": dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8", cache_scale=0.5),
-    "mlra4-fp8b": dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8b"),
+    "mlra4": dict(_MLRA4, dtype="bf16"),
+    "mla": dict(_MLA, dtype="bf16"),
+    "tp-share": dict(_TP4, dtype="bf16"),
+    "mlra2": dict(_MLRA2, dtype="bf16"),
+    "mlra4-k2": dict(_MLRA4, dtype="bf16", blocks_per_head=2),
+    "mlra4-k4": dict(_MLRA4, dtype="bf16", blocks_per_head=4),
+    "mlra2-tp2": dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"),
+    "mlra4-fp8": dict(_MLRA4, dtype="fp8", cache_scale=0.5),
+    "mla-fp8": dict(_MLA, dtype="fp8", cache_scale=0.25),
+    "tp-share-fp8": dict(_TP4, dtype="fp8", cache_scale=1.0),
+    "mlra2-fp8": dict(_MLRA2, dtype="fp8", cache_scale=1.25),
+    "mlra4-fp8b": dict(_MLRA4, dtype="fp8b"),
+    "mla-fp8b": dict(_MLA, dtype="fp8b"),
+    "tp-share-fp8b": dict(_TP4, dtype="fp8b"),
+    "mlra2-fp8b": dict(_MLRA2, dtype="fp8b"),
 }
+
+
+def _variant_heads(s):
+    return sorted({0, s.n_heads // 4 + 1, s.n_heads - 1})
 
 
 @pytest.mark.parametrize("page_size", [16, 64])
 @pytest.mark.parametrize("name", list(VARIANT_SHAPES))
-def test_variants_many_short_sequences(name, page_size):
-    """Forty sequences of 0..300 tokens on every tuned kernel variant: many
-    tiles that start or end mid-page, empty and one-token sequences.
-
-    Outputs are compared sequence by sequence against that sequence's own RMS:
-    a short sequence averages few latent rows, so its outputs are several times
-    larger than a long one's and a batch-wide RMS would judge them on the wrong
-    scale (a numpy emulation of only the kernel's bf16 roundings of q~ and P
-    reaches 2.55e-2 of the batch RMS on this input at page size 64, and 1.3e-2
-    of the sequence RMS)."""
-    _say(f"case: variant {name}, page size {page_size}")
+def test_variants_units_span_sequences(name, page_size):
+    """Every tuned kernel on a batch of short sequences (0..300 tokens, empty
+    and one-token ones among them) sized from the device's work units so that
+    there are at least three tiles per unit: units start and end mid-sequence
+    and many cover three or more sequences (the page-id gather's fallback, the
+    in-loop query reload, partials of several sequences per unit)."""
+    s0 = synth.Shape(batch=1, page_size=page_size, **VARIANT_SHAPES[name])
+    units, tt = _gpu.plan_geometry(s0)
     rng = np.random.default_rng(500 + page_size)
-    lens = [int(v) for v in rng.integers(0, 300, 40)]
+    lens = []
+    tiles = 0
+    while tiles < 3 * units:
+        n = int(rng.integers(0, 300))
+        lens.append(n)
+        tiles += (n + tt - 1) // tt
     lens[3] = 0
     lens[17] = 1
     lens[30] = 0
+    _say(f"case: variant {name}, page size {page_size}: {len(lens)} sequences, {units} units of {tt}-token tiles")
     s = synth.Shape(batch=len(lens), page_size=page_size, **VARIANT_SHAPES[name])
     inp = synth.make_inputs(s, ("list", lens), 600 + len(name))
-    heads = sorted({0, s.n_heads // 4 + 1, s.n_heads // 2 + 6, s.n_heads - 1})
-    pairs = [(b, i) for b in range(s.batch) for i in heads]
     prob = _gpu.GpuProblem(inp)
     out, l = prob.run()
-    ref, rl = oracle.decode_unabsorbed(inp, pairs)
-    g = np.stack([out[b, i] for b, i in pairs])
-    _gpu.check_lse(np.stack([l[b, i] for b, i in pairs]), rl, s.dtype)
-    worst = 0.0
-    for b in range(s.batch):
-        rows = [k for k, (bb, _) in enumerate(pairs) if bb == b]
-        if lens[b] == 0:
-            assert np.all(g[rows] == 0), f"sequence {b} is empty but has non-zero outputs"
-            continue
-        worst = max(worst, _gpu.check_outputs(g[rows], ref[rows], s.dtype, f"sequence {b} (n={lens[b]})"))
-    _say(f"  max err / sequence rms {worst:.2e}")
+    assert mlra.read_flags(prob.ws) == 0
+    pairs = [(b, i) for b in range(s.batch) for i in _variant_heads(s)]
+    err = _compare(inp, out, l, pairs)
+    _say(f"  max err / rms {err:.2e}")
+
+
+@pytest.mark.parametrize("name", list(VARIANT_SHAPES))
+def test_variants_unit_starts_on_last_tile(name):
+    """A work unit whose first tile is the last tile of one sequence and whose
+    other tiles are all of the next sequence (a two-tile prologue moves the
+    load cursor past the first sequence before the unit's page ids are
+    gathered): the lengths are chosen from the device's units U and tile size
+    T so that unit U / 4 covers tile U, the last of sequence 0 (partial), and
+    the three tiles of sequence 1. Every head of sequence 1 and sampled heads
+    of the long sequences 0 and 2 against the oracle; no page flagged."""
+    s0 = synth.Shape(batch=1, **VARIANT_SHAPES[name])
+    units, tt = _gpu.plan_geometry(s0)
+    assert units % 4 == 0
+    lens = [tt * units + 5, 3 * tt - 7, tt * (3 * units - 4)]
+    tiles = [(n + tt - 1) // tt for n in lens]
+    n_tiles = sum(tiles)
+    u = units // 4
+    assert _gpu.tile_begin(u, n_tiles, units) == tiles[0] - 1
+    assert _gpu.tile_begin(u + 1, n_tiles, units) == tiles[0] + tiles[1]
+    _say(f"case: variant {name}: unit {u} of {units} covers tiles [{tiles[0] - 1}, {tiles[0] + tiles[1]}), "
+         f"lengths {lens}")
+    s = synth.Shape(batch=3, **VARIANT_SHAPES[name])
+    inp = synth.make_inputs(s, ("list", lens), 800 + len(name))
+    prob = _gpu.GpuProblem(inp)
+    out, l = prob.run()
+    assert mlra.read_flags(prob.ws) == 0
+    pairs = [(1, i) for i in range(s.n_heads)] + [(b, i) for b in (0, 2) for i in (0, s.n_heads - 1)]
+    err = _compare(inp, out, l, pairs)
+    _say(f"  max err / rms {err:.2e}")
