@@ -57,7 +57,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int W_, int DR_, int NBR_, int HT_, int G_, int TT_, int OCC_, bool F8_ = false, bool CF_ = false,
-          int CS_ = 1, bool P2_ = false, bool TS_ = false, int HPW_ = 1>
+          int CS_ = 1, bool P2_ = false, bool TS_ = false, int HPW_ = 1, bool QL_ = false>
 struct Cfg {
   static constexpr int W = W_;      // latent block width
   static constexpr int DR = DR_;    // RoPE key width
@@ -99,9 +99,9 @@ struct Cfg {
   static constexpr int TASKS = NBR * HT / HPW;
   static constexpr int NWAVES = TASKS * G * CS;
   static constexpr int NTHREADS = NWAVES * 64;
-  // waves per SIMD when OCC workgroups share a compute unit (the second
-  // __launch_bounds__ argument, which bounds the registers per wave)
-  static constexpr int WAVES_PER_SIMD = OCC * NWAVES / 4 > 1 ? OCC * NWAVES / 4 : 1;
+  // waves per SIMD when OCC workgroups share a compute unit, rounded up (the
+  // second __launch_bounds__ argument, which bounds the registers per wave)
+  static constexpr int WAVES_PER_SIMD = (OCC * NWAVES + 3) / 4;
   static constexpr int TILE_BYTES = TT * ROWB;
   static constexpr int TILE_CHUNKS = TT * CPRG;  // HBM chunks of one tile
   // Loader threads: the largest multiple of 64 not above NTHREADS that divides
@@ -124,7 +124,12 @@ struct Cfg {
   // registers for the lo parts of one head tile (bf16 caches): the wave's
   // latent k-steps (the first KKC without column splits; with them the share
   // depends on the wave's split)
-  static constexpr int NLO = F8 ? 1 : (CS > 1 ? KKH : KKC);
+  // QL (bf16 caches): the lo parts live in LDS instead of registers, one
+  // 1 KB row (64 lanes x 16 bytes) per (task, head tile, latent k-step), read
+  // next to the tile operands; for kernels whose registers are full
+  static constexpr bool QL = QL_ && !F8;
+  static constexpr int NLO = (F8 || QL) ? 1 : (CS > 1 ? KKH : KKC);
+  static constexpr int QLO_BYTES = QL ? TASKS * HPW * KKC * 1024 : 0;
   static constexpr int NSUB = TT / 32;
   static constexpr int SUBW = NSUB / G;          // 32-token sub-tiles per wave per tile
   static constexpr int NQ = W / 128 / CS;        // 128-column groups per wave on the value side
@@ -132,7 +137,7 @@ struct Cfg {
   static constexpr int SEQ_WIN = 64;
   static constexpr int XCH_BYTES = CS > 1 ? NWAVES * 64 * 8 * 4 : 0;  // partial-score exchange
   static constexpr int PT_CAP_RAW =
-      (160 * 1024 / OCC - 2 * TILE_BYTES - SEQ_WIN * 4 - NWAVES * 64 - XCH_BYTES - 256) / 4;
+      (160 * 1024 / OCC - 2 * TILE_BYTES - SEQ_WIN * 4 - NWAVES * 64 - XCH_BYTES - QLO_BYTES - 256) / 4;
   static constexpr int PT_CAP = PT_CAP_RAW > 4096 ? 4096 : PT_CAP_RAW;
   static_assert(ROWB % 128 == 0, "rows must be whole 128-byte groups (the LDS swizzle)");
   static_assert(W % (128 * CS) == 0 && DR % 32 == 0 && KK % CS == 0, "");
@@ -236,6 +241,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   __shared__ int32_t seq_end[C::SEQ_WIN];  // cum[lo + 1 + i]
   __shared__ float amax_sh[C::CS > 1 ? C::NWAVES : 1][16];  // segment ends: row maxima of the column splits
   __shared__ float xch[C::CS > 1 ? C::NWAVES : 1][8][64];     // partial scores of the column splits
+  __shared__ __attribute__((aligned(16))) uint8_t qlo[C::QL ? C::QLO_BYTES : 16];  // QL: lo query parts
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -399,7 +405,15 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
         if (head_ok[hw]) v = gload16(qe + off);
         Qb[hw][u] = v;
-        if constexpr (!C::F8) {
+        if constexpr (C::QL) {
+          // every wave of a task writes the same values into its rows, before
+          // any of them reads them (a new sequence starts after the tile barrier)
+          if (lat) {
+            u32x4_t vl = u32x4_t{0u, 0u, 0u, 0u};
+            if (head_ok[hw]) vl = gload16(qe + 2 * C::W + off);
+            *reinterpret_cast<u32x4_t*>(qlo + ((task * HW + hw) * C::KKC + kk) * 1024 + 16 * lane) = vl;
+          }
+        } else if constexpr (!C::F8) {
           if (u < C::NLO) {
             u32x4_t vl = u32x4_t{0u, 0u, 0u, 0u};
             if (head_ok[hw] && lat) vl = gload16(qe + 2 * C::W + off);
@@ -594,7 +608,13 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
                 S0[hw] = mfma_bf16(A0[u], Qb[hw][kl], S0[hw]);
                 S1[hw] = mfma_bf16(A1[u], Qb[hw][kl], S1[hw]);
               }
-              if constexpr (!C::F8) {
+              if constexpr (C::QL) {
+                if (lat) {
+                  const u32x4_t ql = lds_read16(qlo + ((task * HW + hw) * C::KKC + cs * C::KKH + kl) * 1024 + 16 * lane);
+                  S0[hw] = mfma_bf16(A0[u], ql, S0[hw]);
+                  S1[hw] = mfma_bf16(A1[u], ql, S1[hw]);
+                }
+              } else if constexpr (!C::F8) {
                 if (kl < C::NLO && lat) {
                   S0[hw] = mfma_bf16(A0[u], Ql[hw][kl], S0[hw]);
                   S1[hw] = mfma_bf16(A1[u], Ql[hw][kl], S1[hw]);
@@ -845,25 +865,27 @@ struct Entry {
 };
 
 template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1,
-          bool P2 = false, bool TS = false, int HPW = 1>
+          bool P2 = false, bool TS = false, int HPW = 1, bool QL = false>
 constexpr Entry entry() {
-  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2, TS, HPW>;
+  using C = Cfg<W, DR, NBR, HT, G, TT, OCC, F8, CF, CS, P2, TS, HPW, QL>;
   return Entry{MfmaVariant{W, DR, NBR, HT, G, TT, OCC, F8 ? (TS ? 2 : 1) : 0, C::NTHREADS, 2 * C::TILE_BYTES},
                &run_variant<C>};
 }
 
 // Shapes with a tuned MFMA kernel. Key: (w, d_r, blocks per row, 16-head tiles per block).
-// Step order (compute-first flag): measured per shape on one box, same
-// binary A/B: compute-first is 4-7% faster for the TP-share, MLRA-2, FP8
-// MLRA-4 and column-split MLA kernels and 2-6% slower for bf16 MLRA-4; the FP8
-// TP-share and MLRA-2 kernels follow their bf16 counterparts. Two-tile
-// prologue (last flag): 4-6% faster for the TP-share and FP8 MLRA-4 kernels,
-// 22% for MLRA-2, slower for bf16 MLRA-4 (3%) and MLA (45%: its registers).
+// Each tuning was chosen by same-box A/B timing of the candidates (step
+// order, prologue, column splits, head tiles per wave, occupancy, where the
+// query's lo parts live). Compute-first is 4-7% faster for the TP shares,
+// MLRA-2, FP8 MLRA-4 and the column-split MLA kernels and 2-6% slower for bf16
+// MLRA-4; the two-tile prologue 4-6% faster for the TP shares and FP8 MLRA-4,
+// 22% for MLRA-2.
 const Entry kVariants[] = {
     entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
     // MLA: one 512 latent, 64 heads; column-split waves (half the value
-    // columns and half the score dimensions each), compute-first
-    entry<512, 64, 1, 4, 1, 32, 1, false, true, 2>(),
+    // columns and half the score dimensions each), compute-first; the lo query
+    // parts in LDS (in registers they spilled 65 VGPRs: 137.5 vs 103.7 us at
+    // B = 32, 8K)
+    entry<512, 64, 1, 4, 1, 32, 1, false, true, 2, false, false, 1, true>(),
     // one MLRA-4 block (a TP rank's share), <= 16 heads: one-wave workgroups,
     // four per compute unit, each streaming its own 32-token tiles (measured
     // 1.8x faster than four waves sharing 128-token tiles at one per unit)
@@ -872,15 +894,18 @@ const Entry kVariants[] = {
     // workgroup per compute unit (no spills), two-tile prologue: the fastest
     // step of the four combinations of split and prologue measured
     entry<256, 64, 2, 2, 1, 32, 1, false, true, 2, true>(),
-    // 4 x 128 latent, <= 32 heads per block (reading B with k = 2): two head
-    // tiles per wave and two token groups of a 64-token tile, eight waves
-    // (measured 3% faster than eight one-tile waves on 32-token tiles)
-    entry<128, 64, 4, 2, 2, 64, 1, false, false, 1, false, false, 2>(),
+    // 4 x 128 latent, <= 32 heads per block (reading B with k = 2): eight
+    // one-tile waves (two head tiles per wave over 64-token tiles spilled 82
+    // VGPRs with the query's lo parts: 113 vs 85.7 us)
+    entry<128, 64, 4, 2, 1, 32, 1>(),
     // 4 x 128 latent, <= 64 heads per block (reading B with k = 4): two head
-    // tiles per wave, eight waves (sixteen one-tile waves had 128 VGPRs each
-    // and spilled; measured 142 -> 82 us at B = 32, 8K)
-    entry<128, 64, 4, 4, 1, 32, 1, false, false, 1, false, false, 2>(),
-    entry<256, 64, 1, 2, 2, 64, 1>(),   // one 256 block + RoPE, <= 32 heads
+    // tiles per wave, eight waves, the lo query parts in LDS (sixteen one-tile
+    // waves spill; 112.8 us with the lo parts in registers, 99.6 in LDS)
+    entry<128, 64, 4, 4, 1, 32, 1, false, false, 1, false, false, 2, true>(),
+    // one MLRA-2 block (a TP-2 rank's share), <= 32 heads: column-split waves,
+    // two workgroups per compute unit, compute-first, two-tile prologue
+    // (406 -> 235 us at B = 64, 32K against one workgroup of four waves)
+    entry<256, 64, 1, 2, 1, 32, 2, false, true, 2, true>(),
     // FP8 (E4M3FN) caches of the same shapes and tunings
     entry<128, 64, 4, 1, 1, 32, 2, true, true, 1, true>(),
     entry<512, 64, 1, 4, 1, 32, 1, true>(),
