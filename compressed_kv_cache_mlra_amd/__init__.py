@@ -8,6 +8,7 @@ every call raises if the library is not built or no GPU is present.
 
 Entry points (same names as the C ABI, without the mlra_ prefix):
   workspace_bytes, append_latent, absorb_query, attend, decode, combine,
+  decode_step, decode_step_noalloc, rope_key, project_query, project_token,
   read_flags, status_string; and the measurement helper stream_read.
 """
 from __future__ import annotations
@@ -22,9 +23,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmlra.so")
 
 F32, BF16, FP8_E4M3, FP8_E4M3_BS = 0, 1, 2, 3
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 7
+ABI_VERSION = 8
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MLRA_NOALLOC_SCRATCH_BYTES
 
 
 class MlraError(RuntimeError):
@@ -82,13 +84,14 @@ def lib() -> ctypes.CDLL:
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.mlra_decode_step.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
+        L.mlra_decode_step_noalloc.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
         L.mlra_read_flags.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
         L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp, ctypes.c_size_t, vp]
         L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
         for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
-                  "mlra_combine", "mlra_read_flags", "mlra_stream_read", "mlra_rope_key",
-                  "mlra_project_query", "mlra_project_token"):
+                  "mlra_combine", "mlra_decode_step", "mlra_decode_step_noalloc", "mlra_read_flags",
+                  "mlra_stream_read", "mlra_rope_key", "mlra_project_query", "mlra_project_token"):
             getattr(L, f).restype = ctypes.c_int
         if L.mlra_abi_version() != ABI_VERSION:
             raise ImportError("libmlra ABI version mismatch; rebuild the library")
@@ -331,6 +334,25 @@ def decode_step(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, w
         _ptr(lse, kind="f32", name="lse", numel=B * H * K, nullable=True),
         _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
         _stream(stream)), "decode_step")
+
+
+def decode_step_noalloc(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, w_uv, out, lse=None,
+                        stream=None):
+    """decode_step with the library's static device scratch as its workspace
+    (for callers that cannot allocate; calls that overlap on one GPU race)."""
+    B, H, K = desc.batch, desc.n_heads, desc.blocks_per_head
+    _check(lib().mlra_decode_step_noalloc(
+        ctypes.byref(desc),
+        _pool_ptr(pool, desc),
+        _ptr(page_table, kind="int32", name="page_table", numel=B * desc.max_pages_per_seq, nullable=True),
+        _ptr(seq_lens, kind="int32", name="seq_lens", numel=B), ctypes.c_int32(int(max_seq_len)),
+        _ptr(q_c, desc, name="q_c", numel=B * H * desc.d_h),
+        _ptr(q_r, desc, name="q_r", numel=B * H * desc.d_r, nullable=desc.d_r == 0),
+        _ptr(w_uk, desc, name="w_uk", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(w_uv, desc, name="w_uv", numel=H * K * _w(desc) * desc.d_h),
+        _ptr(out, kind="f32", name="out", numel=B * H * desc.d_h),
+        _ptr(lse, kind="f32", name="lse", numel=B * H * K, nullable=True),
+        _stream(stream)), "decode_step_noalloc")
 
 
 def read_flags(workspace, stream=None) -> int:

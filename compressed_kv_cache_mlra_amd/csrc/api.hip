@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mlra.h"
 #include "common.h"
 #include "launch.h"
@@ -172,6 +175,37 @@ CombineArgs combine_args(const mlra_desc* d, const Plan& p, const void* ws, cons
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLRA_OK : MLRA_ERR_HIP; }
 
+// ------------------------------------------------------- allocation-free step
+// The workspace of mlra_decode_step_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends. Host code
+// never uses the array's name as an address: the device address of each GPU's
+// copy is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept here.
+constexpr size_t kScratchBytes = MLRA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch copy.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLRA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLRA_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLRA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MLRA_OK;
+}
+
 // Element type of queries, weights and append inputs (bf16 for FP8 caches).
 int arrays_dtype(const mlra_desc* d) { return fp8_mode(d) ? MLRA_BF16 : d->dtype; }
 
@@ -182,7 +216,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 7; }
+int mlra_abi_version(void) { return 8; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -191,6 +225,7 @@ const char* mlra_status_string(int status) {
     case MLRA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MLRA_ERR_WORKSPACE: return "workspace too small";
     case MLRA_ERR_HIP: return "HIP runtime error";
+    case MLRA_ERR_SCRATCH: return "shape needs more workspace than the static scratch (MLRA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -275,6 +310,22 @@ int mlra_decode_step(const mlra_desc* desc, const void* pool, const int32_t* pag
   st = mlra_decode(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, workspace, ws_bytes, stream);
   if (st != MLRA_OK) return st;
   return hip_status(launch_combine(c, arrays_dtype(desc), static_cast<hipStream_t>(stream)));
+}
+
+int mlra_decode_step_noalloc(const mlra_desc* desc, const void* pool, const int32_t* page_table,
+                             const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
+                             const void* w_uk, const void* w_uv, float* out, float* lse, void* stream) {
+  const size_t need = mlra_workspace_bytes(desc, max_seq_len);
+  if (need == 0) return MLRA_ERR_INVALID_ARG;
+  if (!pool || !seq_lens || !q_c || !w_uk || !w_uv || !out || (desc->d_r > 0 && !q_r)) return MLRA_ERR_INVALID_ARG;
+  if (need > kScratchBytes) return MLRA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_of_current_device(&ws);
+  if (st != MLRA_OK) return st;
+  // nothing in the workspace has to start at zero: each step writes its plan
+  // and header before anything reads them
+  return mlra_decode_step(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, w_uv, out, lse, ws,
+                          kScratchBytes, stream);
 }
 
 int mlra_append_latent(const mlra_desc* desc, void* pool, const int32_t* page_table,

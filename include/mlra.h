@@ -28,8 +28,9 @@
  *  - Every pointer argument is a caller-owned DEVICE pointer (except `desc`,
  *    which is host memory read during the call). Arrays are dense, row-major,
  *    16-byte aligned. The library allocates nothing and keeps no state across
- *    calls; it is safe to call from several host threads on different streams
- *    with different workspaces.
+ *    calls (the one exception is the static scratch of
+ *    mlra_decode_step_noalloc, below); it is safe to call from several host
+ *    threads on different streams with different workspaces.
  *  - `stream` is a hipStream_t (NULL = the default stream). All work is
  *    enqueued on it asynchronously; results are ready when the stream is.
  *  - Element type: every floating-point input (pool, queries, weights, x,
@@ -79,7 +80,9 @@ typedef enum {
   MLRA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape */
   MLRA_ERR_UNSUPPORTED = -2, /* a shape or dtype this build has no kernel for */
   MLRA_ERR_WORKSPACE = -3,   /* workspace smaller than mlra_workspace_bytes() */
-  MLRA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  MLRA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  MLRA_ERR_SCRATCH = -5      /* mlra_decode_step_noalloc: the shape's workspace exceeds
+                                MLRA_NOALLOC_SCRATCH_BYTES */
 } mlra_status;
 
 typedef enum { MLRA_F32 = 0, MLRA_BF16 = 1, MLRA_FP8_E4M3 = 2, MLRA_FP8_E4M3_BS = 3 } mlra_dtype;
@@ -200,6 +203,28 @@ int mlra_decode_step(const mlra_desc* desc, const void* pool, const int32_t* pag
                      const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
                      const void* w_uk, const void* w_uv, float* out, float* lse, void* workspace,
                      size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch of mlra_decode_step_noalloc. */
+#define MLRA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* mlra_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors minus the workspace, which is a
+ * static device array of MLRA_NOALLOC_SCRATCH_BYTES inside the library (one
+ * copy per GPU the library runs on, held until the process ends; its device
+ * address is looked up on the first call on each device). The call allocates
+ * nothing and frees nothing. Shapes whose mlra_workspace_bytes(desc,
+ * max_seq_len) exceeds MLRA_NOALLOC_SCRATCH_BYTES return MLRA_ERR_SCRATCH
+ * before anything is enqueued. Every call on one GPU uses that GPU's single
+ * scratch copy: calls that overlap in time on one GPU (different streams or
+ * host threads without ordering between them) race and give undefined results;
+ * calls ordered on one stream are safe. Nothing in the scratch needs to start
+ * at zero: each step writes its plan before reading it. The error flags of the
+ * step (MLRA_FLAG_*) live in the scratch and cannot be read back through
+ * mlra_read_flags. */
+int mlra_decode_step_noalloc(const mlra_desc* desc, const void* pool, const int32_t* page_table,
+                             const int32_t* seq_lens, int32_t max_seq_len, const void* q_c, const void* q_r,
+                             const void* w_uk, const void* w_uv, float* out, float* lse, void* stream);
 
 /* RoPE key of the new token (the decoupled key of lesty.tech section 4,
  * computed from the token's hidden state and rotated for its position):

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert mlra.lib().mlra_abi_version() == mlra.ABI_VERSION
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert mlra.status_string(code) != "unknown status"
     assert mlra.status_string(7) == "unknown status"
 
@@ -158,6 +158,30 @@ def test_decode_step_validation():
     assert step(ws_bytes=need - 1) == mlra.ERR_WORKSPACE
     assert L.mlra_decode_step(None, FAKE, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                               ctypes.c_size_t(need), None) == mlra.ERR_INVALID_ARG
+
+
+def test_decode_step_noalloc_validation():
+    """The allocation-free step validates like mlra_decode_step and rejects a
+    shape whose workspace exceeds the static scratch, all before any HIP call."""
+    L = mlra.lib()
+    d = _desc()
+
+    def step(desc=d, pool=FAKE, seq_lens=FAKE, max_seq_len=100, q_c=FAKE, q_r=FAKE, w_uk=FAKE, w_uv=FAKE,
+             out=FAKE, lse=None):
+        return L.mlra_decode_step_noalloc(ctypes.byref(desc), pool, None, seq_lens, max_seq_len, q_c, q_r, w_uk,
+                                          w_uv, out, lse, None)
+
+    for field in ("pool", "seq_lens", "q_c", "q_r", "w_uk", "w_uv", "out"):
+        assert step(**{field: None}) == mlra.ERR_INVALID_ARG, field
+    assert step(max_seq_len=-1) == mlra.ERR_INVALID_ARG
+    assert step(max_seq_len=4 * 64 + 1) == mlra.ERR_INVALID_ARG
+    assert L.mlra_decode_step_noalloc(None, FAKE, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                      None) == mlra.ERR_INVALID_ARG
+    big = _desc(batch=4096, n_heads=64, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="bf16", max_pages_per_seq=1,
+                num_pages=4096)
+    assert mlra.workspace_bytes(big, 64) > mlra.NOALLOC_SCRATCH_BYTES
+    assert step(desc=big, max_seq_len=64) == mlra.ERR_SCRATCH
+    assert "scratch" in mlra.status_string(mlra.ERR_SCRATCH)
 
 
 def test_project_token_validation():
