@@ -11,10 +11,14 @@ serve the cache stream.
 Prints one JSON line. `value` is decode tokens/s (batch / step time over K
 steps timed back to back with one event pair around all of them). The
 `roofline` object reports the attention kernel (the one that streams the cache):
-algorithmic cache bytes per launch / its mean duration from HIP events recorded
-around every launch on the launch stream, over a second pass of the same K
-steps, against the 8 TB/s HBM3E peak. `cpu_baseline` times the CPU oracle (test infrastructure, used
-here only for this baseline) on a bounded sample of the same workload.
+algorithmic cache bytes per launch / its mean duration over a second pass of the
+same K steps, each attention launch dispatched with a HIP event pair that its
+dispatch fills with the kernel's own start and stop times (mlra_attend_timed),
+against the 8 TB/s HBM3E peak; `roofline.trace` gives the same ratio from the
+committed rocprofv3 kernel-trace summary of this workload when that summary was
+taken on the current attention source. `cpu_baseline` times the CPU oracle
+(test infrastructure, used here only for this baseline) on a bounded sample of
+the same workload, and on the tiny fp32 workload with one thread.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -36,16 +40,21 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/s + latent-cache HBM GB/s (% of peak), MLRA-4 B=32 ctx=8K, 1 GPU"
-KERNEL_SOURCE = os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", "attend_mfma.hip")
-# rocprofv3 counter summaries of the attention kernel, per workload
-PROFILE_TAGS = {2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
+# the attention kernels' sources: a committed profile counts for the current
+# build only when it was taken on these exact files
+KERNEL_SOURCES = [os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", f)
+                  for f in ("attend_mfma.hip", "attend_generic.hip", "common.h")]
+# rocprofv3 summaries of the attention kernel, per workload:
+# profiles/attend_<tag>_kernel_stats.txt (kernel trace) and _counters.txt (HBM bytes)
+PROFILE_TAGS = {1: "tiny_fp32", 2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
                 5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k", 7: "mlra4_b32_ctx8k_layer",
-                8: "mlra4_fp8_block_scaled_b32_ctx8k"}
+                8: "mlra4_fp8_block_scaled_b32_ctx8k", 9: "readb_k2_b32_ctx8k", 10: "readb_k4_b32_ctx8k",
+                11: "h24_b32_ctx8k", 12: "h24_readb_k4_b32_ctx8k", 13: "tp2share_mlra2_b64_ctx32k"}
 
 
-def _counters_file(workload: int) -> str:
+def _profile_file(workload: int, kind: str) -> str:
     tag = PROFILE_TAGS.get(workload, "none")
-    return os.path.join(ROOT, "profiles", f"attend_mfma_{tag}_counters.txt")
+    return os.path.join(ROOT, "profiles", f"attend_{tag}_{kind}.txt")
 COPY_BYTES = 1 << 30
 
 
@@ -80,19 +89,45 @@ def _copy_calibration(steps: int):
 
 
 def _source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _profile_text(workload: int, kind: str):
+    """A committed profile summary of this workload, if it was taken on the
+    current attention source."""
+    path = _profile_file(workload, kind)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != _source_hash():
+        return None
+    return text
+
+
+def _trace(bytes_alg: float, workload: int):
+    """The attention kernel's mean duration in the committed rocprofv3
+    kernel-trace summary of this workload (same source) and the HBM fraction
+    it gives."""
+    text = _profile_text(workload, "kernel_stats")
+    m = text and re.search(r"attend_trace_mean_ns:\s*([0-9.eE+]+)", text)
+    if not m:
+        return None
+    ns = float(m.group(1))
+    gbps = bytes_alg / (ns * 1e-9) / 1e9
+    return {"mean_us": round(ns / 1e3, 3), "achieved": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "source": os.path.relpath(_profile_file(workload, "kernel_stats"), ROOT)}
 
 
 def _traffic(bytes_alg: float, workload: int):
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
     counter summary of this workload, when it was taken on the current kernel
     source."""
-    path = _counters_file(workload)
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or m.group(1) != _source_hash():
+    text = _profile_text(workload, "counters")
+    if text is None:
         return None
     f = re.search(r"hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", text)
     w = re.search(r"hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -165,9 +200,10 @@ def main():
     stream = torch.cuda.current_stream()
     setup_s = time.time() - t0
 
-    def launch(i, cs, mark=lambda k: None):
+    def launch(i, cs, mark=lambda k: None, kev=None):
         """One step on pool instance i % pools, enqueued on cs; mark(k) is
-        called at the kernel boundaries 0 (start) .. 4 (end)."""
+        called at the kernel boundaries 0 (start) .. 4 (end); kev: an event
+        pair that the attention's dispatch fills with its own start and stop."""
         p = i % len(pools)
         mark(0)
         if qpath:
@@ -180,13 +216,16 @@ def main():
             mlra.append_latent(desc, pools[p], page_table, positions, x, w_dkv[p], kr_new, None, ws, cs)
         mlra.absorb_query(desc, seq_lens, q_c, q_r, w_uk, ws, cs)
         mark(2)
-        mlra.attend(desc, pools[p], page_table, ws, cs)
+        if kev is None:
+            mlra.attend(desc, pools[p], page_table, ws, cs)
+        else:
+            mlra.attend_timed(desc, pools[p], page_table, ws, kev[0], kev[1], cs)
         mark(3)
         mlra.combine(desc, ws, w_uv, out, None, cs)
         mark(4)
 
-    def step(i, ev=None):
-        launch(i, stream, (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None))
+    def step(i, ev=None, kev=None):
+        launch(i, stream, (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None), kev)
 
     for i in range(args.warmup):
         step(i)
@@ -205,12 +244,20 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # Timed region 2: the same K steps with HIP events around every launch on the
-    # launch stream, for the per-kernel durations and the attention roofline.
+    # launch stream (per-kernel durations, each including its dispatch).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
+    # Timed region 3: the same K steps, the attention dispatched with an event
+    # pair that records the kernel's own start and stop (the roofline's
+    # duration); no other events in these steps.
+    kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, None, kevs[i])
+    torch.cuda.synchronize()
+    attend_kernel_ms = [k[0].elapsed_time(k[1]) for k in kevs]
     qp_ms = [e[0].elapsed_time(e[1]) for e in evs] if qpath else [0.0]
     pre_ms = [e[1 if qpath else 0].elapsed_time(e[2]) for e in evs]
     attend_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -227,7 +274,7 @@ def main():
     heads_per_block = s.n_heads * s.blocks_per_head // s.n_blocks
     # per token: every (head, attended block) pair scores w + d_r and accumulates w
     attn_flops = float(n_tokens) * s.n_heads * s.blocks_per_head * (4.0 * s.w + 2.0 * s.d_r)
-    attend_mean_ms = float(np.mean(attend_ms))
+    attend_mean_ms = float(np.mean(attend_kernel_ms))
     achieved = cache_bytes / (attend_mean_ms * 1e-3) / 1e9
     tokens_per_s = s.batch / (ms_per_step * 1e-3)
 
@@ -256,15 +303,19 @@ def main():
         "stream_read_gbps_same_device": None if read_gbps is None else round(read_gbps, 1),
         "attend_frac_of_stream_read": None if read_gbps is None else round(achieved / read_gbps, 4),
         "cache_pct_of_hbm_peak_full_step": round(100.0 * cache_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "attend_kernel_us": {"mean": round(1e3 * attend_mean_ms, 2),
+                             "p10": round(1e3 * float(np.percentile(attend_kernel_ms, 10)), 2),
+                             "p50": round(1e3 * float(np.percentile(attend_kernel_ms, 50)), 2),
+                             "p90": round(1e3 * float(np.percentile(attend_kernel_ms, 90)), 2)},
         "kernel_us_with_events": {"append_absorb": round(1e3 * float(np.mean(pre_ms)), 2),
-                      "attend": round(1e3 * attend_mean_ms, 2),
+                      "attend": round(1e3 * float(np.mean(attend_ms)), 2),
                       "attend_p50": round(1e3 * float(np.percentile(attend_ms, 50)), 2),
                       "attend_p10": round(1e3 * float(np.percentile(attend_ms, 10)), 2),
                       "attend_p90": round(1e3 * float(np.percentile(attend_ms, 90)), 2),
                       "combine": round(1e3 * float(np.mean(comb_ms)), 2),
                       "token_projections": round(1e3 * float(np.mean(qp_ms)), 2) if qpath else None},
         "roofline": {
-            "kernel": "attend_mfma_kernel",
+            "kernel": "attend_generic_kernel" if s.dtype == "f32" else "attend_mfma_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -272,6 +323,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes_per_launch": cache_bytes,
             "algorithmic_flops_per_launch": attn_flops,
+            "duration": "kernel start to stop recorded by its dispatch (mlra_attend_timed), mean over K whole steps",
+            "trace": _trace(cache_bytes, args.workload),
             "traffic": _traffic(cache_bytes, args.workload),
             "mfma_tflops": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12, 2),
             "mfma_frac_of_bf16_peak": round(attn_flops / (attend_mean_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -288,6 +341,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"]["one_thread_tiny"] = _cpu_one_thread_tiny()
     print(json.dumps(result), flush=True)
 
 
@@ -357,6 +411,27 @@ def _cpu_baseline(inp, target_s: float):
             "kind": "oracle",
             "sample": f"{done} of {s.batch} sequences, all {s.n_heads} heads each "
                       f"({tokens} cached tokens), un-absorbed fp64 oracle, {spent:.1f} s"}
+
+
+def _cpu_one_thread_tiny(target_s: float = 2.0):
+    """The oracle on one thread over the whole tiny fp32 workload (every head
+    of its one 256-token sequence), repeated for about target_s seconds."""
+    import oracle
+    import synth
+
+    inp = synth.workload_inputs(1)
+    n0 = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while reps == 0 or time.perf_counter() - t0 < target_s:
+            oracle.decode_unabsorbed(inp)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    finally:
+        oracle.set_num_threads(n0)
+    return {"workload": synth.WORKLOADS[1]["name"], "us_per_step": round(dt * 1e6, 1),
+            "tokens_per_s": round(inp.shape.batch / dt, 1), "cores": 1, "steps_timed": reps}
 
 
 if __name__ == "__main__":

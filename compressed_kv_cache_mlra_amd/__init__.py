@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(HERE, "libmlra.so")
 F32, BF16, FP8_E4M3, FP8_E4M3_BS = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 FLAG_BAD_PAGE = 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 NOALLOC_SCRATCH_BYTES = 32 << 20  # MLRA_NOALLOC_SCRATCH_BYTES
 
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, vp]
         L.mlra_absorb_query.argtypes = [dp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mlra_attend.argtypes = [dp, vp, ip, vp, ctypes.c_size_t, vp]
+        L.mlra_attend_timed.argtypes = [dp, vp, ip, vp, ctypes.c_size_t, vp, vp, vp]
         L.mlra_decode.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.mlra_combine.argtypes = [dp, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.mlra_decode_step.argtypes = [dp, vp, ip, ip, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
@@ -89,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.mlra_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         L.mlra_rope_key.argtypes = [dp, vp, vp, ip, vp, vp, ctypes.c_size_t, vp]
         L.mlra_project_query.argtypes = [dp, vp, vp, vp, vp, ip, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_decode",
+        for f in ("mlra_append_latent", "mlra_absorb_query", "mlra_attend", "mlra_attend_timed", "mlra_decode",
                   "mlra_combine", "mlra_decode_step", "mlra_decode_step_noalloc", "mlra_read_flags",
                   "mlra_stream_read", "mlra_rope_key", "mlra_project_query", "mlra_project_token"):
             getattr(L, f).restype = ctypes.c_int
@@ -290,6 +291,22 @@ def attend(desc, pool, page_table, workspace, stream=None):
              nullable=True),
         _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
         _stream(stream)), "attend")
+
+
+def attend_timed(desc, pool, page_table, workspace, start, stop, stream=None):
+    """Measurement helper: attend, with the kernel's own start and stop times
+    recorded into the torch.cuda.Event pair (start, stop) by its dispatch."""
+    for e in (start, stop):
+        if e.cuda_event == 0:  # torch creates the HIP event on its first record
+            e.record(_torch().cuda.current_stream() if stream is None else stream)
+    _check(lib().mlra_attend_timed(
+        ctypes.byref(desc),
+        _pool_ptr(pool, desc),
+        _ptr(page_table, kind="int32", name="page_table", numel=desc.batch * desc.max_pages_per_seq,
+             nullable=True),
+        _ptr(workspace, kind="bytes", name="workspace"), ctypes.c_size_t(workspace.numel()),
+        ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event),
+        _stream(stream)), "attend_timed")
 
 
 def decode(desc, pool, page_table, seq_lens, max_seq_len, q_c, q_r, w_uk, workspace, stream=None):

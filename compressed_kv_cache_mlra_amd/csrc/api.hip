@@ -216,7 +216,7 @@ using namespace mlra;
 
 extern "C" {
 
-int mlra_abi_version(void) { return 8; }
+int mlra_abi_version(void) { return 9; }
 
 const char* mlra_status_string(int status) {
   switch (status) {
@@ -263,6 +263,20 @@ int mlra_attend(const mlra_desc* desc, const void* pool, const int32_t* page_tab
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.variant) return hip_status(launch_attend_mfma(p.variant, a, s));
   return hip_status(launch_attend_generic(a, desc->dtype, s));
+}
+
+int mlra_attend_timed(const mlra_desc* desc, const void* pool, const int32_t* page_table, void* workspace,
+                      size_t ws_bytes, void* start_event, void* stop_event, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != MLRA_OK) return st;
+  if (!pool || !workspace || !start_event || !stop_event) return MLRA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return MLRA_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(desc, p, pool, page_table, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t t0 = static_cast<hipEvent_t>(start_event), t1 = static_cast<hipEvent_t>(stop_event);
+  if (p.variant) return hip_status(launch_attend_mfma(p.variant, a, s, t0, t1));
+  return hip_status(launch_attend_generic(a, desc->dtype, s, t0, t1));
 }
 
 int mlra_decode(const mlra_desc* desc, const void* pool, const int32_t* page_table,

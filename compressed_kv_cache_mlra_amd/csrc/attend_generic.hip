@@ -5,6 +5,8 @@
 // section 5, with the MLRA block split of the alanhou.org "Core Mechanism").
 // One wave per (unit, head-block pair); lane t scores token t of a 64-token
 // tile, then the wave accumulates the latent columns, lane c owning column c.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -143,13 +145,21 @@ __global__ __launch_bounds__(64) void attend_generic_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_attend_generic(const DecodeArgs& a, int dtype, hipStream_t stream) {
+hipError_t launch_attend_generic(const DecodeArgs& a, int dtype, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid(a.units, a.n_heads * a.k);
   const size_t sh = sizeof(float) * (a.w + a.d_r + TT + 2) + sizeof(int64_t) * TT + 16;
-  if (dtype == 1)
-    attend_generic_kernel<uint16_t, float><<<grid, 64, sh, stream>>>(a);
-  else
-    attend_generic_kernel<float, float><<<grid, 64, sh, stream>>>(a);
+  // with events, the dispatch records the kernel's own start and stop times
+  if (dtype == 1) {
+    if (t0 || t1)
+      hipExtLaunchKernelGGL(attend_generic_kernel<uint16_t, float>, grid, dim3(64), sh, stream, t0, t1, 0, a);
+    else
+      attend_generic_kernel<uint16_t, float><<<grid, 64, sh, stream>>>(a);
+  } else {
+    if (t0 || t1)
+      hipExtLaunchKernelGGL(attend_generic_kernel<float, float>, grid, dim3(64), sh, stream, t0, t1, 0, a);
+    else
+      attend_generic_kernel<float, float><<<grid, 64, sh, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

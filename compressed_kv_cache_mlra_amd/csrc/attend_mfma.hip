@@ -42,6 +42,8 @@
 //    by a power of two into [1, 2), 11 significant bits) and P in fp16; with
 //    block scales the value side takes P s 2^-E (E a running exponent of the
 //    largest scale, folded back into the partial's max).
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -854,14 +856,17 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
 }
 
 template <class C>
-hipError_t run_variant(const DecodeArgs& a, hipStream_t stream) {
-  attend_mfma_kernel<C><<<a.units, C::NTHREADS, 0, stream>>>(a);
+hipError_t run_variant(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (t0 || t1)  // the dispatch records the kernel's own start and stop times
+    hipExtLaunchKernelGGL(attend_mfma_kernel<C>, dim3(a.units), dim3(C::NTHREADS), 0, stream, t0, t1, 0, a);
+  else
+    attend_mfma_kernel<C><<<a.units, C::NTHREADS, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 struct Entry {
   MfmaVariant v;
-  hipError_t (*fn)(const DecodeArgs&, hipStream_t);
+  hipError_t (*fn)(const DecodeArgs&, hipStream_t, hipEvent_t, hipEvent_t);
 };
 
 template <int W, int DR, int NBR, int HT, int G, int TT, int OCC, bool F8 = false, bool CF = false, int CS = 1,
@@ -928,9 +933,10 @@ const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tile
   return nullptr;
 }
 
-hipError_t launch_attend_mfma(const MfmaVariant* v, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_attend_mfma(const MfmaVariant* v, const DecodeArgs& a, hipStream_t stream, hipEvent_t t0,
+                              hipEvent_t t1) {
   for (const Entry& e : kVariants)
-    if (&e.v == v) return e.fn(a, stream);
+    if (&e.v == v) return e.fn(a, stream, t0, t1);
   return hipErrorInvalidValue;
 }
 

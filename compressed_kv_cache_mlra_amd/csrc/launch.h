@@ -25,11 +25,15 @@ const MfmaVariant* find_mfma_variant(int w, int d_r, int n_blocks, int head_tile
 hipError_t launch_absorb(const DecodeArgs& a, int dtype, bool q_bf16, const int32_t* seq_lens,
                          const void* q_c, const void* q_r, const void* w_uk, hipStream_t stream);
 
-hipError_t launch_attend_mfma(const MfmaVariant* v, const DecodeArgs& a, hipStream_t stream);
+// t0, t1 (optional): events that the dispatch fills with the kernel's own
+// start and stop times (measurement helper mlra_attend_timed)
+hipError_t launch_attend_mfma(const MfmaVariant* v, const DecodeArgs& a, hipStream_t stream,
+                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Generic VALU attention for any supported shape (fp32 or bf16 cache).
 constexpr int kGenericTileTokens = 64;
-hipError_t launch_attend_generic(const DecodeArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attend_generic(const DecodeArgs& a, int dtype, hipStream_t stream, hipEvent_t t0 = nullptr,
+                                 hipEvent_t t1 = nullptr);
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 

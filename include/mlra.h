@@ -297,6 +297,16 @@ int mlra_read_flags(const void* workspace, size_t ws_bytes, uint32_t* flags, voi
  * or a sink that is too small. Asynchronous on `stream`. */
 int mlra_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
+/* Measurement helper, not part of the decode path: mlra_attend, with the
+ * attention kernel dispatched through hipExtLaunchKernel so that start_event
+ * and stop_event (hipEvent_t, created by the caller) receive the kernel's own
+ * start and stop times, as a kernel trace would, rather than the times at
+ * which the stream reached two event markers around the launch. Same
+ * arguments, results and errors as mlra_attend, plus MLRA_ERR_INVALID_ARG for
+ * a NULL event. */
+int mlra_attend_timed(const mlra_desc* desc, const void* pool, const int32_t* page_table, void* workspace,
+                      size_t ws_bytes, void* start_event, void* stop_event, void* stream);
+
 /* Text for a status code. Never NULL. */
 const char* mlra_status_string(int status);
 

@@ -89,6 +89,8 @@ def lib():
         L.oracle_decode_flops_bytes.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int32
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int32]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -263,3 +265,7 @@ def decode_flops_bytes(n, heads_u, w_u, d_r, elem_bytes=2.0):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))

@@ -470,6 +470,14 @@ void oracle_decode_flops_bytes(double n, double heads_u, double w_u, double d_r,
   *bytes = elem_bytes * n * (w_u + d_r);
 }
 
+void oracle_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int32_t oracle_num_threads(void) {
 #ifdef _OPENMP
   return (int32_t)omp_get_max_threads();

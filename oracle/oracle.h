@@ -160,6 +160,8 @@ void oracle_decode_flops_bytes(double n, double heads_u, double w_u, double d_r,
 
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int32_t oracle_num_threads(void);
+/* Sets that number (n > 0; for timing the oracle on fewer threads). */
+void oracle_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }

@@ -184,6 +184,20 @@ def test_decode_step_noalloc_validation():
     assert "scratch" in mlra.status_string(mlra.ERR_SCRATCH)
 
 
+def test_attend_timed_validation():
+    """The timed attention helper validates like mlra_attend and needs both events."""
+    L = mlra.lib()
+    d = _desc()
+    need = mlra.workspace_bytes(d, 100)
+
+    def call(pool=FAKE, ws=FAKE, ws_bytes=need, t0=FAKE, t1=FAKE):
+        return L.mlra_attend_timed(ctypes.byref(d), pool, None, ws, ctypes.c_size_t(ws_bytes), t0, t1, None)
+
+    for field in ("pool", "ws", "t0", "t1"):
+        assert call(**{field: None}) == mlra.ERR_INVALID_ARG, field
+    assert call(ws_bytes=need - 1) == mlra.ERR_WORKSPACE
+
+
 def test_project_token_validation():
     L = mlra.lib()
     d = _desc(d_model=64, d_cq=32, dtype="bf16")
