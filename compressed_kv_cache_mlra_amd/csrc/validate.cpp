@@ -1,8 +1,6 @@
 // Host-side descriptor validation of libmlra.
 #include "validate.h"
 
-#include "common.h"
-
 #include <math.h>
 #include <stdint.h>
 
@@ -24,6 +22,8 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   if (d->batch < 1 || d->n_heads < 1 || d->d_h < 1 || d->d_c < 1 || d->n_blocks < 1 ||
       d->blocks_per_head < 1 || d->d_r < 0 || d->max_pages_per_seq < 1 || d->num_pages < 1)
     return MLRA_ERR_INVALID_ARG;
+  // widths bounded before any arithmetic on them (no int overflow below)
+  if (d->d_c > kMaxLatent || d->d_r > 512 || d->d_h > 512) return MLRA_ERR_UNSUPPORTED;
   if (d->d_c % d->n_blocks != 0) return MLRA_ERR_INVALID_ARG;
   if (d->n_blocks % d->blocks_per_head != 0) return MLRA_ERR_INVALID_ARG;
   const int groups = d->n_blocks / d->blocks_per_head;  // head groups
@@ -31,8 +31,8 @@ int check_desc(const mlra_desc* d, ShapeInfo* s) {
   const int ps = d->page_size;
   if (ps < 16 || ps > 256 || (ps & (ps - 1)) != 0) return MLRA_ERR_INVALID_ARG;
   const int elem = d->dtype == MLRA_F32 ? 4 : 2;
-  const int row = d->d_c + d->d_r;
-  if ((static_cast<int64_t>(row) * elem) % 16 != 0) return MLRA_ERR_INVALID_ARG;
+  const int64_t row = static_cast<int64_t>(d->d_c) + d->d_r;
+  if ((row * elem) % 16 != 0) return MLRA_ERR_INVALID_ARG;
   const int w = d->d_c / d->n_blocks;
   if (d->dtype != MLRA_F32 && (w % 8 != 0 || d->d_r % 8 != 0)) return MLRA_ERR_INVALID_ARG;
   // FP8 rows: d_c code bytes in whole 16-byte chunks, then the bf16 RoPE key

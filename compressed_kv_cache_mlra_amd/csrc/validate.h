@@ -6,6 +6,9 @@
 
 namespace mlra {
 
+constexpr int kMaxBatch = 4096;    // sequences per call (the plan keeps them in LDS)
+constexpr int kMaxLatent = 65536;  // latent width d_c of a cache row
+
 struct ShapeInfo {
   int w;           // latent block width d_c / n_blocks
   int hpb;         // heads per block h k / b

@@ -94,7 +94,7 @@ typedef struct {
   int32_t batch;             /* B, number of sequences (1 .. 4096) */
   int32_t n_heads;           /* h */
   int32_t d_h;               /* query / value head width (1 .. 512) */
-  int32_t d_c;               /* latent width stored in each cache row */
+  int32_t d_c;               /* latent width stored in each cache row (1 .. 65536) */
   int32_t n_blocks;          /* b: latent blocks per row (1 = MLA); divides d_c */
   int32_t blocks_per_head;   /* k: blocks each head attends (divides b) */
   int32_t d_r;               /* RoPE key width (0 .. 512) */

@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MLRA_ORACLE_LIB: another build of oracle.c to load (the sanitizer test's)
+_LIB_PATH = os.environ.get("MLRA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, FP8, FP8_BS = 0, 1, 2, 3
 METHODS = {"MHA": 0, "MQA": 1, "GQA": 2, "MLA": 3, "MFA": 4, "TPA": 5, "MLRA": 6}
