@@ -485,7 +485,7 @@ def _variant_heads(s):
 def test_variants_units_span_sequences(name, page_size):
     """Every tuned kernel on a batch of short sequences (0..300 tokens, empty
     and one-token ones among them) sized from the device's work units so that
-    there are at least three tiles per unit: units start and end mid-sequence
+    there are at least five tiles per unit: units start and end mid-sequence
     and many cover three or more sequences (the page-id gather's fallback, the
     in-loop query reload, partials of several sequences per unit)."""
     s0 = synth.Shape(batch=1, page_size=page_size, **VARIANT_SHAPES[name])
@@ -493,7 +493,7 @@ def test_variants_units_span_sequences(name, page_size):
     rng = np.random.default_rng(500 + page_size)
     lens = []
     tiles = 0
-    while tiles < 3 * units:
+    while tiles < 5 * units:
         n = int(rng.integers(0, 300))
         lens.append(n)
         tiles += (n + tt - 1) // tt
@@ -516,14 +516,15 @@ def test_variants_unit_starts_on_last_tile(name):
     """A work unit whose first tile is the last tile of one sequence and whose
     other tiles are all of the next sequence (a two-tile prologue moves the
     load cursor past the first sequence before the unit's page ids are
-    gathered): the lengths are chosen from the device's units U and tile size
-    T so that unit U / 4 covers tile U, the last of sequence 0 (partial), and
-    the three tiles of sequence 1. Every head of sequence 1 and sampled heads
-    of the long sequences 0 and 2 against the oracle; no page flagged."""
+    gathered): with U units and T-token tiles, 3 U tiles in all (three per
+    unit: the plain balanced split), unit U / 4 covers tile 3 U / 4, the last
+    of sequence 0 (partial), and the two tiles of sequence 1. Every head of
+    sequence 1 and sampled heads of the long sequences 0 and 2 against the
+    oracle; no page flagged."""
     s0 = synth.Shape(batch=1, **VARIANT_SHAPES[name])
     units, tt = _gpu.plan_geometry(s0)
     assert units % 4 == 0
-    lens = [tt * units + 5, 3 * tt - 7, tt * (3 * units - 4)]
+    lens = [tt * (3 * units // 4) + 5, 2 * tt - 7, tt * (9 * units // 4 - 3)]
     tiles = [(n + tt - 1) // tt for n in lens]
     n_tiles = sum(tiles)
     u = units // 4
