@@ -20,7 +20,10 @@ taken on the current attention source. `cpu_baseline` times the CPU oracle
 (test infrastructure, used here only for this baseline) on a bounded sample of
 the same workload, and on the tiny fp32 workload with one thread.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+The W warm-up steps are followed by more untimed steps until --warmup-seconds
+(0.5 s) of wall time has passed, so the timed steps run at settled clocks.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--workload 2]
 """
 from __future__ import annotations
 
@@ -63,6 +66,9 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup-seconds", type=float, default=0.5,
+                   help="keep running untimed steps after the W warm-up steps until this much wall time has "
+                        "passed (the GPU's clocks take about 0.1 s of load to settle; 0 for counter runs)")
     p.add_argument("--workload", type=int, default=2, choices=list(range(1, 14)))
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
@@ -227,9 +233,17 @@ def main():
     def step(i, ev=None, kev=None):
         launch(i, stream, (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None), kev)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # Warm-up: W steps, then more untimed steps in chunks until the floor of
+    # wall time has passed. From idle the first ~0.1 s of steps run up to 10%
+    # slower while the clocks rise; the timed steps should see steady clocks.
+    t_warm = time.time()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        for _ in range(args.warmup if warm_steps < args.warmup else 50):
+            step(warm_steps)
+            warm_steps += 1
+        torch.cuda.synchronize()
+    warm_s = time.time() - t_warm
 
     # Timed region 1: K whole steps back to back, bracketed by two events only
     # (events between the kernels would add their own packets to the step).
@@ -293,6 +307,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -169,6 +169,17 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __attribute__((address_space(4))) const int32_t cint32_t;
 __device__ __forceinline__ int32_t cload(const int32_t* p) { return *(cint32_t*)(p); }
 
+// Work unit of workgroup b in a grid of n. The dispatcher deals workgroups to
+// the 8 XCDs in turn (b -> XCD b % 8); numbering units XCD-major puts runs of
+// consecutive units, which share a sequence's query rows, page-table row and
+// partial slots, on one XCD and its L2. XCD x runs units
+// [x*q + min(x, r), (x+1)*q + min(x+1, r)) with q = n / 8, r = n % 8: a
+// bijection for any n.
+__device__ __forceinline__ int xcd_major_unit(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 __device__ __forceinline__ floatx4_t mfma_bf16(u32x4_t a, u32x4_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WAVES_PER_SIMD) void attend_mfma_ke
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
   const int32_t* cum = reinterpret_cast<const int32_t*>(a.ws + a.off_cum);
   const int32_t* nlen = reinterpret_cast<const int32_t*>(a.ws + a.off_nlen);
-  const int unit = blockIdx.x;
+  const int unit = xcd_major_unit(blockIdx.x, gridDim.x);
   // The unit's descriptor from the plan (one scalar fetch): tile range, the
   // sequence owning its first tile and that sequence's tile range and length.
   const int32_t* ud = reinterpret_cast<const int32_t*>(a.ws + a.off_udesc) + unit * kUnitDescInts;
