@@ -911,9 +911,11 @@ const Entry kVariants[] = {
     // step of the four combinations of split and prologue measured
     entry<256, 64, 2, 2, 1, 32, 1, false, true, 2, true>(),
     // 4 x 128 latent, <= 32 heads per block (reading B with k = 2): eight
-    // one-tile waves (two head tiles per wave over 64-token tiles spilled 82
-    // VGPRs with the query's lo parts: 113 vs 85.7 us)
-    entry<128, 64, 4, 2, 1, 32, 1>(),
+    // one-tile waves, compute-first, two-tile prologue (82.6 -> 61.5 us at
+    // B = 32, 8K against store-first with a one-tile prologue; two head tiles
+    // per wave spilled 82 VGPRs over 64-token tiles, and at 32-token tiles
+    // with the lo parts in LDS measured 75.7 us)
+    entry<128, 64, 4, 2, 1, 32, 1, false, true, 1, true>(),
     // 4 x 128 latent, <= 64 heads per block (reading B with k = 4): two head
     // tiles per wave, eight waves, the lo query parts in LDS (sixteen one-tile
     // waves spill; 112.8 us with the lo parts in registers, 99.6 in LDS)
