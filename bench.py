@@ -52,7 +52,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "compressed_kv_cache_mlra_amd", "csrc", f)
 PROFILE_TAGS = {1: "tiny_fp32", 2: "mlra4_b32_ctx8k", 3: "mla_b32_ctx8k", 4: "tpshare_b64_ctx32k",
                 5: "mlra2_ragged_append", 6: "mlra4_fp8_b32_ctx8k", 7: "mlra4_b32_ctx8k_layer",
                 8: "mlra4_fp8_block_scaled_b32_ctx8k", 9: "readb_k2_b32_ctx8k", 10: "readb_k4_b32_ctx8k",
-                11: "h24_b32_ctx8k", 12: "h24_readb_k4_b32_ctx8k", 13: "tp2share_mlra2_b64_ctx32k"}
+                11: "h24_b32_ctx8k", 12: "h24_readb_k4_b32_ctx8k", 13: "tp2share_mlra2_b64_ctx32k",
+                14: "mla_tpshare_b64_ctx32k"}
 
 
 def _profile_file(workload: int, kind: str) -> str:
@@ -69,7 +70,7 @@ def _args():
     p.add_argument("--warmup-seconds", type=float, default=0.5,
                    help="keep running untimed steps after the W warm-up steps until this much wall time has "
                         "passed (the GPU's clocks take about 0.1 s of load to settle; 0 for counter runs)")
-    p.add_argument("--workload", type=int, default=2, choices=list(range(1, 14)))
+    p.add_argument("--workload", type=int, default=2, choices=list(range(1, 15)))
     p.add_argument("--pools", type=int, default=3, help="cache pool instances rotated per step")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -920,6 +920,12 @@ const Entry kVariants[] = {
     // tiles per wave, eight waves, the lo query parts in LDS (sixteen one-tile
     // waves spill; 112.8 us with the lo parts in registers, 99.6 in LDS)
     entry<128, 64, 4, 4, 1, 32, 1, false, false, 1, false, false, 2, true>(),
+    // MLA's share under 4-way tensor parallelism: the whole 512 latent and the
+    // RoPE key for <= 16 heads; column-split waves, two workgroups per compute
+    // unit, compute-first, two-tile prologue (362.7 us at B = 64, 32K; 446.4
+    // store-first with a one-tile prologue, 422.4 with 64-token tiles in two
+    // token groups at one workgroup per unit)
+    entry<512, 64, 1, 1, 1, 32, 2, false, true, 2, true>(),
     // one MLRA-2 block (a TP-2 rank's share), <= 32 heads: column-split waves,
     // two workgroups per compute unit, compute-first, two-tile prologue
     // (406 -> 235 us at B = 64, 32K against one workgroup of four waves)

@@ -159,6 +159,12 @@ WORKLOADS = {
     13: dict(name="MLRA-2 one TP-2 rank share, bf16, B=64 h=32 d_h=128 d_c=256 d_r=64 ctx=32768 paged",
              shape=Shape(batch=64, n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"),
              lengths=("fixed", 32768)),
+    # MLA's share under the same 4-way tensor parallelism as workload 4: the
+    # latent cannot be split, so each rank reads the whole 512 + 64 row for its
+    # 16 heads (the one-GPU stand-in for the MLRA-against-MLA decode comparison)
+    14: dict(name="MLA one TP-4 rank share, bf16, B=64 h=16 d_h=128 d_c=512 d_r=64 ctx=32768 paged",
+             shape=Shape(batch=64, n_heads=16, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="bf16"),
+             lengths=("fixed", 32768)),
 }
 
 

@@ -27,6 +27,8 @@ SMALL = {
     5: (dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="bf16"), [100, 0, 333]),
     # the TP-2 share of MLRA-2: one 256-wide block serving 32 heads
     13: (dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"), [7, 64, 65, 1000, 3001]),
+    # MLA's TP-4 rank share: the whole 512 latent for 16 heads
+    14: (dict(n_heads=16, d_h=128, d_c=512, n_blocks=1, d_r=64, dtype="bf16"), [3, 64, 97, 1500, 2049]),
 }
 
 
@@ -75,7 +77,7 @@ def test_workload1_full_fp32():
     _say(f"workload 1 max rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("wl", [2, 3, 4, 5, 13])
+@pytest.mark.parametrize("wl", [2, 3, 4, 5, 13, 14])
 def test_small_all_outputs(wl):
     kw, lens = SMALL[wl]
     _say(f"case: small shape of workload {wl}, lengths {lens}")
@@ -85,7 +87,7 @@ def test_small_all_outputs(wl):
     _say(f"workload {wl} small: max err/rms {err:.2e}")
 
 
-@pytest.mark.parametrize("wl", [2, 3, 4, 13])
+@pytest.mark.parametrize("wl", [2, 3, 4, 13, 14])
 def test_full_size_first_last_all_heads(wl):
     """Full-size workloads as the benchmark launches them: every head of the
     first and the last sequence, and sampled pairs, against the oracle."""
@@ -465,6 +467,7 @@ VARIANT_SHAPES = {
     "mlra4-k2": dict(_MLRA4, dtype="bf16", blocks_per_head=2),
     "mlra4-k4": dict(_MLRA4, dtype="bf16", blocks_per_head=4),
     "mlra2-tp2": dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="bf16"),
+    "mla-tp-share": dict(_MLA, n_heads=16, dtype="bf16"),
     "mlra4-fp8": dict(_MLRA4, dtype="fp8", cache_scale=0.5),
     "mla-fp8": dict(_MLA, dtype="fp8", cache_scale=0.25),
     "tp-share-fp8": dict(_TP4, dtype="fp8", cache_scale=1.0),
