@@ -246,17 +246,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 // combine_kernel; the work is laid out so that a workgroup needs two dependent
 // memory round trips (unit ranges, then all partial slots at once):
 //   * one workgroup per (head, 4 sequences), 256 threads;
-//   * merge: item = (sequence, 4 latent columns, half); the two halves of an
-//     item take alternate partial slots (up to kFastSlots each per batch) and
-//     are merged with one lane exchange;
-//   * product: thread = (8 output columns, row residue r mod 16); its W^UV
-//     rows are requested with 16-byte loads before the merge starts; each
-//     wave multiplies its rows on MFMA and the four waves are summed in LDS.
+//   * merge: item = (sequence, K / 32 latent columns, half), one per thread;
+//     the two halves of an item take alternate partial slots (a batch of
+//     slots per half in flight at once) and are merged with one lane exchange;
+//   * product: thread = (8 output columns, row residue r mod 16); its first
+//     16 W^UV rows are requested with 16-byte loads before the merge starts,
+//     each further batch before the previous one is multiplied (both before
+//     the merge would hold too many registers for two workgroups per unit);
+//     each wave
+//     multiplies its rows on MFMA and the four waves are summed in LDS.
 constexpr int kFastThreads = 256;
 // sequences per workgroup (a multiple of 4; 8 measured slower on every
 // workload: fewer workgroups outweigh the fewer W^UV re-reads)
 constexpr int kFastSeq = 4;
-constexpr int kFastSlots = 12;  // partial slots per half whose loads are in flight together
+constexpr int kFastSlots = 12;  // partial slots per half in flight together, 4-column items
 constexpr int kFastDh = 128;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -267,11 +270,18 @@ static_assert(kFastSeq % 4 == 0 && kFastSeq <= 16, "sequences are MFMA rows, fou
 template <int W, int KB, bool PB>
 __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs a) {
   constexpr int K = W * KB;               // merged latent columns per head
-  constexpr int CG = K / 4;               // 4-column groups per sequence
-  constexpr int NITEMS = kFastSeq * CG * 2;
-  static_assert(NITEMS % kFastThreads == 0, "merge items must fill the workgroup");
+  // merge item = (sequence, CW latent columns, half): every thread holds one
+  // item, so all partial slots of a batch are requested in one round trip
+  constexpr int CW = K * kFastSeq * 2 / kFastThreads;
+  static_assert(CW >= 4 && CW % 4 == 0 && W % CW == 0, "whole 4-column loads inside one block");
+  constexpr int CG = K / CW;              // column groups per sequence
+  // partial slots per half whose loads are in flight together (the loaded
+  // values take CW / 2 registers a slot)
+  constexpr int NSL = CW <= 4 ? kFastSlots : (CW <= 8 ? 8 : 6);
   constexpr int ROWS = K / 16;            // W^UV rows per thread
   constexpr int RB = ROWS < 16 ? ROWS : 16;  // rows per load batch
+  constexpr int NBAT = ROWS / RB;         // load batches, double-buffered
+  static_assert(ROWS % RB == 0, "");
   __shared__ __attribute__((aligned(16))) float ot[K][kFastSeq];        // merged latents, transposed
   __shared__ __attribute__((aligned(16))) float red[4][16][8][kFastSeq];  // per-wave partial outputs
 
@@ -281,13 +291,14 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
   const int b0 = blockIdx.y * kFastSeq;
   const int nb = min(kFastSeq, a.batch - b0);
 
-  // ---- W^UV rows of this thread: e = rr + 16 i, columns [8 dc, 8 dc + 8)
+  // ---- W^UV rows of this thread: e = rr + 16 i, columns [8 dc, 8 dc + 8);
+  // the first batch is requested before the merge
   const int dc = tid & 15, rr = tid >> 4;
   const uint16_t* wuv = static_cast<const uint16_t*>(a.w_uv) + static_cast<int64_t>(head) * K * kFastDh + 8 * dc;
   typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
-  u32x4_t wr[RB];
+  u32x4_t wr[2][RB];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) wr[i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * i) * kFastDh);
+  for (int i = 0; i < RB; ++i) wr[0][i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * i) * kFastDh);
 
   typedef __attribute__((address_space(4))) const int32_t cint32_t;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
@@ -300,79 +311,74 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
   const int64_t empty_hk = static_cast<int64_t>(a.empty_slot) * a.hk;
 
   // ---- merge
-  // lse values are stored after the outputs: a store issued here would be
+  // the lse value is stored after the outputs: a store issued here would be
   // waited for (stores count in vmcnt) before the W^UV registers are used
-  constexpr int NIT = NITEMS / kFastThreads;
-  float lse_v[NIT];
-  int64_t lse_i[NIT];
+  float lse_v = 0.f;
+  int64_t lse_i = -1;
   auto merge = [&](auto check_units) __attribute__((always_inline)) {
     constexpr bool kCheck = decltype(check_units)::value;
+    const int half = tid & 1;
+    const int cgi = (tid >> 1) % CG, bl = (tid >> 1) / CG;
+    const int e = CW * cgi, jj = e / W, c = e % W;
+    const int b = min(b0 + bl, a.batch - 1);  // rows past the batch merge a real sequence, unused
+    const int hk = head * KB + jj;
+    const int2 su = *reinterpret_cast<const int2*>(sunit + 2 * b);  // first, last unit
+    const int nslots = (su.y - su.x + 1) * G;
+    float M = -INFINITY, L = 0.f;
+    float acc[CW];
 #pragma unroll
-    for (int it0 = 0; it0 < NITEMS; it0 += kFastThreads) {
-      const int it = it0 + tid;
-      const int half = it & 1;
-      const int cgi = (it >> 1) % CG, bl = (it >> 1) / CG;
-      const int e = 4 * cgi, jj = e / W, c = e % W;
-      const int b = min(b0 + bl, a.batch - 1);  // rows past the batch merge a real sequence, unused
-      const int hk = head * KB + jj;
-      const int2 su = *reinterpret_cast<const int2*>(sunit + 2 * b);  // first, last unit
-      const int nslots = (su.y - su.x + 1) * G;
-      float M = -INFINITY, L = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s0 = half; s0 < nslots; s0 += 2 * kFastSlots) {
-        float ms[kFastSlots], ls[kFastSlots];
-        float4 vs[kFastSlots];
+    for (int q = 0; q < CW; ++q) acc[q] = 0.f;
+    for (int s0 = half; s0 < nslots; s0 += 2 * NSL) {
+      float ms[NSL], ls[NSL];
+      float4 vs[NSL][CW / 4];
 #pragma unroll
-        for (int u = 0; u < kFastSlots; ++u) {
-          const int sl = s0 + 2 * u;
-          const int32_t uu = su.x + sl / G;
-          const bool ok = sl < nslots && (!kCheck || unit_owns_tiles(uu, NT, units));
-          const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + sl % G) * a.hk + hk : empty_hk + hk;
-          ms[u] = pm[idx];
-          ls[u] = pl[idx];
-          vs[u] = load_partial4<PB>(po, idx * W + c);
-        }
-        float mb = M;
+      for (int u = 0; u < NSL; ++u) {
+        const int sl = s0 + 2 * u;
+        const int32_t uu = su.x + sl / G;
+        const bool ok = sl < nslots && (!kCheck || unit_owns_tiles(uu, NT, units));
+        const int64_t idx = ok ? (static_cast<int64_t>(uu + b) * G + sl % G) * a.hk + hk : empty_hk + hk;
+        ms[u] = pm[idx];
+        ls[u] = pl[idx];
 #pragma unroll
-        for (int u = 0; u < kFastSlots; ++u) mb = fmaxf(mb, ms[u]);
-        const float mu = mb == -INFINITY ? 0.f : mb;
-        const float r = fast_exp2(M - mu);
-        L *= r;
-        acc.x *= r;
-        acc.y *= r;
-        acc.z *= r;
-        acc.w *= r;
-#pragma unroll
-        for (int u = 0; u < kFastSlots; ++u) {
-          const float wgt = fast_exp2(ms[u] - mu);  // 0 for empty slots (m = -inf)
-          L += wgt * ls[u];
-          acc.x += wgt * vs[u].x;
-          acc.y += wgt * vs[u].y;
-          acc.z += wgt * vs[u].z;
-          acc.w += wgt * vs[u].w;
-        }
-        M = mb;
+        for (int q = 0; q < CW / 4; ++q) vs[u][q] = load_partial4<PB>(po, idx * W + c + 4 * q);
       }
-      // merge the two halves (lanes 2q and 2q+1)
-      const float Mo = __shfl_xor(M, 1), Lo = __shfl_xor(L, 1);
-      const float4 ao = make_float4(__shfl_xor(acc.x, 1), __shfl_xor(acc.y, 1), __shfl_xor(acc.z, 1),
-                                    __shfl_xor(acc.w, 1));
-      const float Mt = fmaxf(M, Mo);
-      const float mu = Mt == -INFINITY ? 0.f : Mt;
-      const float r0 = fast_exp2(M - mu), r1 = fast_exp2(Mo - mu);
-      const float Lt = L * r0 + Lo * r1;
-      const float invL = nslots > 0 ? 1.f / Lt : 0.f;
-      lse_i[it0 / kFastThreads] = -1;
-      if (half == 0) {
-        if (c == 0 && a.lse && bl < nb) {
-          lse_i[it0 / kFastThreads] = (static_cast<int64_t>(b) * a.n_heads + head) * KB + jj;
-          lse_v[it0 / kFastThreads] = nslots > 0 ? 0.69314718055994531f * (Mt + __log2f(Lt)) : -INFINITY;
+      float mb = M;
+#pragma unroll
+      for (int u = 0; u < NSL; ++u) mb = fmaxf(mb, ms[u]);
+      const float mu = mb == -INFINITY ? 0.f : mb;
+      const float r = fast_exp2(M - mu);
+      L *= r;
+#pragma unroll
+      for (int q = 0; q < CW; ++q) acc[q] *= r;
+#pragma unroll
+      for (int u = 0; u < NSL; ++u) {
+        const float wgt = fast_exp2(ms[u] - mu);  // 0 for empty slots (m = -inf)
+        L += wgt * ls[u];
+#pragma unroll
+        for (int q = 0; q < CW / 4; ++q) {
+          acc[4 * q + 0] += wgt * vs[u][q].x;
+          acc[4 * q + 1] += wgt * vs[u][q].y;
+          acc[4 * q + 2] += wgt * vs[u][q].z;
+          acc[4 * q + 3] += wgt * vs[u][q].w;
         }
-        ot[e + 0][bl] = (acc.x * r0 + ao.x * r1) * invL;
-        ot[e + 1][bl] = (acc.y * r0 + ao.y * r1) * invL;
-        ot[e + 2][bl] = (acc.z * r0 + ao.z * r1) * invL;
-        ot[e + 3][bl] = (acc.w * r0 + ao.w * r1) * invL;
       }
+      M = mb;
+    }
+    // merge the two halves (lanes 2t and 2t+1)
+    const float Mo = __shfl_xor(M, 1), Lo = __shfl_xor(L, 1);
+    const float Mt = fmaxf(M, Mo);
+    const float mu = Mt == -INFINITY ? 0.f : Mt;
+    const float r0 = fast_exp2(M - mu), r1 = fast_exp2(Mo - mu);
+    const float Lt = L * r0 + Lo * r1;
+    const float invL = nslots > 0 ? 1.f / Lt : 0.f;
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const float ao = __shfl_xor(acc[q], 1);
+      if (half == 0) ot[e + q][bl] = (acc[q] * r0 + ao * r1) * invL;
+    }
+    if (half == 0 && c == 0 && a.lse && bl < nb) {
+      lse_i = (static_cast<int64_t>(b) * a.n_heads + head) * KB + jj;
+      lse_v = nslots > 0 ? 0.69314718055994531f * (Mt + __log2f(Lt)) : -INFINITY;
     }
   };
   if (NT >= units)
@@ -393,11 +399,13 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
 #pragma unroll
   for (int j = 0; j < 8; ++j) pacc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i0 = 0; i0 < ROWS; i0 += RB) {
-    if (i0 > 0) {
+  for (int bt = 0; bt < NBAT; ++bt) {
+    const int i0 = bt * RB;
+    // the next batch is requested before this one is multiplied
+    if (bt + 1 < NBAT) {
 #pragma unroll
       for (int i = 0; i < RB; ++i)
-        wr[i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * (i0 + i)) * kFastDh);
+        wr[(bt + 1) & 1][i] = *(const gu32x4_t*)(wuv + static_cast<int64_t>(rr + 16 * (i0 + RB + i)) * kFastDh);
     }
 #pragma unroll
     for (int s8 = 0; s8 < RB; s8 += 8) {
@@ -419,7 +427,8 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
         u32x4_t bv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) bv[u] = __builtin_amdgcn_perm(wr[s8 + 2 * u + 1][j >> 1], wr[s8 + 2 * u][j >> 1], sel);
+        for (int u = 0; u < 4; ++u)
+          bv[u] = __builtin_amdgcn_perm(wr[bt & 1][s8 + 2 * u + 1][j >> 1], wr[bt & 1][s8 + 2 * u][j >> 1], sel);
         pacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ahi),
                                                           __builtin_bit_cast(bf16x8_t, bv), pacc[j], 0, 0, 0);
         pacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, alo),
@@ -446,9 +455,7 @@ __global__ __launch_bounds__(kFastThreads) void combine_fast_kernel(CombineArgs 
       a.out[(static_cast<int64_t>(b0 + bl) * a.n_heads + head) * kFastDh + d] = a.out_scale * v;
     }
   }
-#pragma unroll
-  for (int i = 0; i < NIT; ++i)
-    if (lse_i[i] >= 0) a.lse[lse_i[i]] = lse_v[i];
+  if (lse_i >= 0) a.lse[lse_i] = lse_v;
 }
 
 template <int W, int KB>

@@ -216,6 +216,20 @@ def test_blocks_per_head_and_head_counts(k, n_blocks, n_heads, d_c):
     _run_and_compare(inp)
 
 
+@pytest.mark.parametrize("k,n_blocks,d_c", [(2, 2, 512), (4, 4, 1024), (2, 2, 1024)])
+def test_combine_wide_heads(k, n_blocks, d_c):
+    """Heads whose merged latent spans 512 or 1024 columns (k blocks of width
+    d_c / b): the specialised combine's wide merge items and its several W^UV
+    load batches, every output against the oracle (these shapes attend on the
+    generic kernel, so the partials are fp32); an empty sequence included."""
+    _say(f"case: wide combine k={k} b={n_blocks} d_c={d_c}")
+    s = synth.Shape(batch=3, n_heads=16, d_h=128, d_c=d_c, n_blocks=n_blocks, d_r=64, dtype="bf16",
+                    blocks_per_head=k)
+    inp = synth.make_inputs(s, ("list", [300, 1, 0]), 91 + k + d_c)
+    _, err = _run_and_compare(inp)
+    _say(f"  max err/rms {err:.2e}")
+
+
 @pytest.mark.parametrize("dtype,d_c,n_blocks,d_r,d_h", [("bf16", 256, 4, 32, 64), ("f32", 512, 4, 64, 128),
                                                         ("bf16", 64, 1, 64, 256)])
 def test_generic_path(dtype, d_c, n_blocks, d_r, d_h):
