@@ -935,11 +935,20 @@ const Entry kVariants[] = {
     entry<512, 64, 1, 4, 1, 32, 1, true>(),
     entry<128, 64, 1, 1, 1, 32, 4, true, true>(),
     entry<256, 64, 2, 2, 1, 32, 2, true, true>(),
+    // FP8 reading B (32 and 64 heads per block) and the TP-2 share of MLRA-2
+    // (no column splits on FP8 caches; MLA's TP-4 share would spill over 500
+    // registers without them and has no FP8 kernel)
+    entry<128, 64, 4, 2, 1, 32, 1, true, true, 1, true>(),
+    entry<128, 64, 4, 4, 1, 32, 1, true, false, 1, false, false, 2>(),
+    entry<256, 64, 1, 2, 1, 32, 2, true, true, 1, true>(),
     // FP8 with one scale per token and latent block (the same tunings)
     entry<128, 64, 4, 1, 1, 32, 2, true, true, 1, true, true>(),
     entry<512, 64, 1, 4, 1, 32, 1, true, false, 1, false, true>(),
     entry<128, 64, 1, 1, 1, 32, 4, true, true, 1, false, true>(),
     entry<256, 64, 2, 2, 1, 32, 2, true, true, 1, false, true>(),
+    entry<128, 64, 4, 2, 1, 32, 1, true, true, 1, true, true>(),
+    entry<128, 64, 4, 4, 1, 32, 1, true, false, 1, false, true, 2>(),
+    entry<256, 64, 1, 2, 1, 32, 2, true, true, 1, true, true>(),
 };
 
 }  // namespace

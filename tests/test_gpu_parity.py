@@ -337,6 +337,13 @@ FP8_SHAPES = {
                  [5, 129, 900, 2049]),
     "mlra2": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=2, d_r=64, dtype="fp8", cache_scale=1.25),
               [100, 0, 333]),
+    # reading B (32 and 64 heads per block) and the TP-2 share of MLRA-2
+    "readb_k2": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8", cache_scale=0.5,
+                      blocks_per_head=2), [40, 257]),
+    "readb_k4": (dict(n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="fp8", cache_scale=0.75,
+                      blocks_per_head=4), [33, 200]),
+    "tp2_share": (dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="fp8", cache_scale=1.0),
+                  [7, 65, 1000]),
 }
 
 
@@ -420,7 +427,7 @@ def test_fp8_append_encodes_kernel_latent():
 def test_fp8b_small_all_outputs(name):
     """Block-scaled FP8 caches (scales 2^u, u in [-3, 1), per token and block;
     NaN codes, keys and scales in unused rows) against the oracle on every
-    output and lse, for each of the four kernel shapes."""
+    output and lse, for each FP8 kernel shape."""
     kw, lens = FP8_SHAPES[name]
     kw = dict(kw, dtype="fp8b")
     kw.pop("cache_scale")
@@ -486,10 +493,16 @@ VARIANT_SHAPES = {
     "mla-fp8": dict(_MLA, dtype="fp8", cache_scale=0.25),
     "tp-share-fp8": dict(_TP4, dtype="fp8", cache_scale=1.0),
     "mlra2-fp8": dict(_MLRA2, dtype="fp8", cache_scale=1.25),
+    "mlra4-k2-fp8": dict(_MLRA4, dtype="fp8", cache_scale=0.5, blocks_per_head=2),
+    "mlra4-k4-fp8": dict(_MLRA4, dtype="fp8", cache_scale=0.5, blocks_per_head=4),
+    "mlra2-tp2-fp8": dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="fp8", cache_scale=1.0),
     "mlra4-fp8b": dict(_MLRA4, dtype="fp8b"),
     "mla-fp8b": dict(_MLA, dtype="fp8b"),
     "tp-share-fp8b": dict(_TP4, dtype="fp8b"),
     "mlra2-fp8b": dict(_MLRA2, dtype="fp8b"),
+    "mlra4-k2-fp8b": dict(_MLRA4, dtype="fp8b", blocks_per_head=2),
+    "mlra4-k4-fp8b": dict(_MLRA4, dtype="fp8b", blocks_per_head=4),
+    "mlra2-tp2-fp8b": dict(n_heads=32, d_h=128, d_c=256, n_blocks=1, d_r=64, dtype="fp8b"),
 }
 
 
