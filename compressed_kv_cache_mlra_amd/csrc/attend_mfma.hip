@@ -896,7 +896,12 @@ constexpr Entry entry() {
 // MLRA-4; the two-tile prologue 4-6% faster for the TP shares and FP8 MLRA-4,
 // 22% for MLRA-2.
 const Entry kVariants[] = {
-    entry<128, 64, 4, 1, 1, 32, 2>(),   // MLRA-4: 4 x 128 latent, <= 16 heads per block
+    // MLRA-4: 4 x 128 latent, <= 16 heads per block; 64-token tiles in two
+    // 32-token groups (eight waves, one workgroup per compute unit),
+    // compute-first (interleaved at B = 32, 8K: step 67.1 -> 64.8 us against
+    // four waves on 32-token tiles at two workgroups per unit; 65.3-65.4 with
+    // the two-tile prologue or store-first)
+    entry<128, 64, 4, 1, 2, 64, 1, false, true>(),
     // MLA: one 512 latent, 64 heads; column-split waves (half the value
     // columns and half the score dimensions each), compute-first; the lo query
     // parts in LDS (in registers they spilled 65 VGPRs: 137.5 vs 103.7 us at
