@@ -242,7 +242,7 @@ def test_generic_path(dtype, d_c, n_blocks, d_r, d_h):
 
 def test_page_sizes():
     _say("case: page sizes")
-    for ps, lens in ((16, [40, 17]), (128, [300, 129]), (256, [513, 5])):
+    for ps, lens in ((16, [40, 17]), (32, [200, 33]), (128, [300, 129]), (256, [513, 5])):
         s = synth.Shape(batch=2, n_heads=64, d_h=128, d_c=512, n_blocks=4, d_r=64, dtype="bf16", page_size=ps)
         inp = synth.make_inputs(s, ("list", lens), 96)
         _run_and_compare(inp)
