@@ -729,7 +729,10 @@ mlra::ProjBatch token_batch(const mlra_desc* d, const void* x, const int32_t* po
 // append, so a column tile covers whole 128-byte lines of each weight row (with
 // two, neighbouring tiles on different XCDs each fetched the shared lines: 36.8
 // MB from HBM for 17.3 MB of weights; 30.8 -> 29.8 us for project_token)
-constexpr int kCplRope = 2, kCplQuery1 = 2, kCplQuery2 = 4, kCplToken = 4;
+// kCplQuery1 likewise (mlra_project_query at the same shape: 28.4 -> 27.8 us);
+// kCplRope stays at two (its 64-column matrix would get fewer workgroups:
+// 10.1 -> 10.9 us with four)
+constexpr int kCplRope = 2, kCplQuery1 = 4, kCplQuery2 = 4, kCplToken = 4;
 
 // Checks the workspace and returns the start of the projection region.
 int proj_scratch(const mlra_desc* d, void* workspace, size_t ws_bytes, void** scratch) {
