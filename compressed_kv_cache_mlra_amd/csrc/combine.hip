@@ -259,7 +259,10 @@ constexpr int kFastThreads = 256;
 // sequences per workgroup (a multiple of 4; 8 measured slower on every
 // workload: fewer workgroups outweigh the fewer W^UV re-reads)
 constexpr int kFastSeq = 4;
-constexpr int kFastSlots = 12;  // partial slots per half in flight together, 4-column items
+// partial slots per half in flight together, 4-column items (eight: step
+// 64.1 -> 63.4 us at MLRA-4 B = 32 8K against twelve, where a sequence has
+// about nine slots, four or five per half)
+constexpr int kFastSlots = 8;
 constexpr int kFastDh = 128;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
